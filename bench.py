@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Throughput of the fused-epilogue GEMM on one MI355X.
+
+Headline workload: C = GELU(A.B + bias), A, B 2048 x 2048 fp16 (N(0,1)/sqrt(2048)),
+bias[2048] fp16 N(0,1), erf-form GELU, fp16 output; fp32 accumulation on the
+matrix cores.  One step = one launch of the fused kernel over one batch of
+resident inputs (the whole hot path: tile mapping, pipelined operand staging,
+MFMA main loop, register epilogue, single write of C).
+
+Timing: W eager warmup launches, then K launches captured in one HIP graph
+(replayed once untimed to upload it), then the timed region: one replay of
+the K-launch graph between torch.cuda.synchronize() calls.  HIP events
+recorded on the launch stream around the same replay give the kernel's
+average duration for the roofline.  Inputs stay resident in HBM, so
+repeated launches see warm L2/MALL, as in the pages' warmup-then-average
+method.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X dense matrix peaks and HBM bandwidth (published); 2516.6 = 256 CU x
+# 4096 fp16 FLOP/clk/CU x 2.4 GHz, i.e. the published 2.5 PFLOP/s.
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6}
+PEAK_HBM_GBS = 8000.0
+HEADLINE = "C3"
+KERNEL_SOURCES = ["dense_gemm_epilogues_tiled_amd/csrc/gemm.hip", "dense_gemm_epilogues_tiled_amd/csrc/device.hpp",
+                  "dense_gemm_epilogues_tiled_amd/csrc/softmax.hip",
+                  "dense_gemm_epilogues_tiled_amd/csrc/config_table.inc"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def time_launches(launch, steps: int, warmup: int, stream):
+    """Returns (wall ms per launch, event ms per launch)."""
+    import torch
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            launch()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(steps):
+            launch()
+    with torch.cuda.stream(stream):
+        g.replay()  # upload, untimed
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
+
+
+def prepare(w, dev):
+    import workloads
+    A, B, bias = workloads.make_inputs(w)
+    return A, B, bias, A.to(dev), B.to(dev), (bias.to(dev) if bias is not None else None)
+
+
+def cpu_baseline(w, A, B, bias):
+    import oracle
+    threads = oracle.default_threads()
+    used = oracle.threads_used(threads)
+    t0 = time.perf_counter()
+    oracle.gemm(A, B, bias, w.M, w.N, w.K, w.dtype, w.epilogue, b_col_major=w.b_col_major, alpha=w.alpha,
+                threads=threads)
+    dt = time.perf_counter() - t0
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": w.flops / dt / 1e12, "unit": "TFLOP/s", "cores": used, "kind": "oracle",
+            "sample": f"the full {w.M}x{w.N}x{w.K} problem once (fp64 triple loop + epilogue, OpenMP over rows)",
+            "seconds": dt, "cpu_model": cpu_model}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-table", action="store_true", help="skip timing the other workloads")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        msg = ("this benchmark runs on one GPU only: the fused GEMM is measured at one GPU's share; "
+               "multi-GPU runs are not part of this build (see the sharding notes in DESIGN.md)")
+        if int(os.environ.get("RANK", "0")) == 0:
+            print(msg, file=sys.stderr)
+        return 2
+
+    import torch
+
+    import dense_gemm_epilogues_tiled_amd as tg
+    import workloads
+
+    tg.load(build_if_missing=False)
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs")
+
+    w = workloads.WORKLOADS[args.workload]
+    A, B, bias, Ad, Bd, bd = prepare(w, dev)
+    out_dtype = torch.float32 if w.epilogue == "softmax" else Ad.dtype
+    Cd = torch.empty((w.M, w.N), dtype=out_dtype, device=dev)
+
+    def launch():
+        tg.gemm(Ad, Bd, bd, epilogue=w.epilogue, b_col_major=w.b_col_major, alpha=w.alpha, out=Cd)
+
+    log(f"timing {w.name}: {w.description}; warmup {args.warmup}, steps {args.steps}")
+    ms_wall, ms_kernel = time_launches(launch, args.steps, args.warmup, stream)
+    tflops = w.flops / (ms_wall * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    achieved = w.flops / (ms_kernel * 1e-3) / 1e12
+    cfg = tg.query_config(w.M, w.N, w.K, Ad.dtype, w.epilogue, w.b_col_major)
+    log(f"{w.name}: {ms_wall * 1e3:.2f} us/launch wall, {ms_kernel * 1e3:.2f} us/launch events, "
+        f"{tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of {peak} TFLOP/s)")
+
+    traffic = measured_traffic(w.name)
+    result = {
+        "metric": "TFLOP/s and % of MFMA peak, fp16 GEMM 2048^3 with fused bias+GELU",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_wall,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if w.dtype == "f16" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.description}", "M": w.M, "N": w.N, "K": w.K,
+                   "epilogue": w.epilogue, "accumulate": "f32", "tile_config": cfg},
+        "pct_of_peak": round(100 * tflops / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel_us": round(ms_kernel * 1e3, 3), "algorithmic_flops_per_launch": w.flops,
+                     "kernel": "gemm_tile_kernel"},
+    }
+
+    if not args.no_table:
+        table = {}
+        for name, wt in workloads.WORKLOADS.items():
+            try:
+                _, _, _, At, Bt, bt = prepare(wt, dev)
+                od = torch.float32 if wt.epilogue == "softmax" else At.dtype
+                Ct = torch.empty((wt.M, wt.N), dtype=od, device=dev)
+
+                def lt(wt=wt, At=At, Bt=Bt, bt=bt, Ct=Ct):
+                    tg.gemm(At, Bt, bt, epilogue=wt.epilogue, b_col_major=wt.b_col_major, alpha=wt.alpha, out=Ct)
+
+                n = 20 if wt.M * wt.N * wt.K > 2 ** 36 else 100
+                wall, ev = time_launches(lt, n, 10, stream)
+                tf = wt.flops / (ev * 1e-3) / 1e12
+                gbs = wt.min_bytes() / (ev * 1e-3) / 1e9
+                table[name] = {"us": round(ev * 1e3, 3), "us_wall": round(wall * 1e3, 3), "TFLOP/s": round(tf, 1),
+                               "pct_mfma_peak": round(100 * tf / PEAK_TFLOPS[wt.dtype], 2),
+                               "GB/s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+                               "tile_config": tg.query_config(wt.M, wt.N, wt.K, At.dtype, wt.epilogue,
+                                                              wt.b_col_major)["id"]}
+                log(f"  {name}: {table[name]}")
+                del At, Bt, bt, Ct
+            except Exception as e:  # keep going: one failing workload must not hide the others
+                table[name] = {"status": f"error: {e}"}
+                log(f"  {name}: error {e}")
+        result["workloads"] = table
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the same workload ...")
+        result["cpu_baseline"] = cpu_baseline(w, A, B, bias)
+        log(f"cpu_baseline: {result['cpu_baseline']}")
+    result["host"] = {"python": platform.python_version(), "torch": torch.__version__,
+                      "hip": getattr(torch.version, "hip", None), "gpu": props.name}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

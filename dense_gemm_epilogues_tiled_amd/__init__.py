@@ -1,0 +1,213 @@
+"""Python binding of libtg.so, the gfx950 fused-epilogue GEMM library.
+
+    C = epilogue(alpha * A.B + bias)      (see include/tg.h)
+
+This module only marshals arguments: every step of the computation runs in
+the HIP kernels of ``libtg.so``.  torch provides device memory and the
+current stream.  The library is loaded after torch so that both use the same
+HIP runtime instance.
+
+Functions named ``tg_*`` mirror the C entry points one to one (they take raw
+integers / pointers and return the status code).  ``gemm`` is the tensor-level
+convenience wrapper: it checks device, dtype, shape and contiguity, allocates
+the output if needed, and raises ``TgError`` on a non-zero status.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (must be imported before libtg.so: shared HIP runtime)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtg.so")
+
+# ---- constants of include/tg.h --------------------------------------------
+TG_OK = 0
+TG_ERR_INVALID_ARG = -1
+TG_ERR_UNSUPPORTED = -2
+TG_ERR_MISALIGNED = -3
+TG_ERR_HIP = -4
+
+TG_DTYPE_F16 = 0
+TG_DTYPE_BF16 = 1
+
+TG_EPI_NONE = 0
+TG_EPI_BIAS = 1
+TG_EPI_BIAS_RELU = 2
+TG_EPI_BIAS_GELU = 3
+TG_EPI_SOFTMAX = 4
+
+TG_KERNEL_GEMM = 0
+TG_KERNEL_GEMM_SOFTMAX = 1
+
+TG_SOFTMAX_MAX_N = 2048
+
+EPILOGUES = {
+    "none": TG_EPI_NONE, "bias": TG_EPI_BIAS, "relu": TG_EPI_BIAS_RELU, "bias_relu": TG_EPI_BIAS_RELU,
+    "gelu": TG_EPI_BIAS_GELU, "bias_gelu": TG_EPI_BIAS_GELU, "softmax": TG_EPI_SOFTMAX,
+}
+DTYPES = {torch.float16: TG_DTYPE_F16, torch.bfloat16: TG_DTYPE_BF16}
+
+
+class tg_tile_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "id", "kind", "bm", "bn", "bk", "stages", "waves", "mfma_m", "mfma_n", "mfma_k", "wave_m", "wave_n",
+        "group_m", "xcd_remap", "lds_bytes", "b_col_major")]
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class tg_gemm_args(ctypes.Structure):
+    _fields_ = [
+        ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("C", ctypes.c_void_p),
+        ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("epilogue", ctypes.c_int32), ("b_col_major", ctypes.c_int32),
+        ("alpha", ctypes.c_float), ("config_id", ctypes.c_int32),
+    ]
+
+
+# Every function include/tg.h declares, with its ctypes signature.
+_SIGNATURES = {
+    "tg_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                               ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "tg_gemm_ex": (ctypes.c_int, [ctypes.POINTER(tg_gemm_args), ctypes.c_void_p]),
+    "tg_gemm_query_config": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, ctypes.POINTER(tg_tile_config)]),
+    "tg_num_configs": (ctypes.c_int, []),
+    "tg_get_config": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(tg_tile_config)]),
+    "tg_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "tg_version": (ctypes.c_int, []),
+}
+
+_lib = None
+
+
+class TgError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {tg_status_string(status)} ({status})" if what else tg_status_string(status))
+
+
+def load(build_if_missing: bool = True):
+    """Load libtg.so (building it first only if no library exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        if not build_if_missing:
+            raise ImportError(f"{LIB_PATH} is missing: run python -m dense_gemm_epilogues_tiled_amd.build")
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+# ---- one-to-one wrappers of the C entry points ------------------------------
+
+def tg_gemm(A: int, B: int, bias: int | None, C: int, M: int, N: int, K: int, dtype: int, epilogue: int,
+            stream: int | None) -> int:
+    return load().tg_gemm(A, B, bias, C, M, N, K, dtype, epilogue, stream)
+
+
+def tg_gemm_ex(args: tg_gemm_args, stream: int | None) -> int:
+    return load().tg_gemm_ex(ctypes.byref(args), stream)
+
+
+def tg_gemm_query_config(M: int, N: int, K: int, dtype: int, epilogue: int, b_col_major: int):
+    """Returns (status, tg_tile_config)."""
+    out = tg_tile_config()
+    rc = load().tg_gemm_query_config(M, N, K, dtype, epilogue, b_col_major, ctypes.byref(out))
+    return rc, out
+
+
+def tg_num_configs() -> int:
+    return load().tg_num_configs()
+
+
+def tg_get_config(index: int):
+    """Returns (status, tg_tile_config)."""
+    out = tg_tile_config()
+    rc = load().tg_get_config(index, ctypes.byref(out))
+    return rc, out
+
+
+def tg_status_string(status: int) -> str:
+    return load().tg_status_string(status).decode()
+
+
+def tg_version() -> int:
+    return load().tg_version()
+
+
+# ---- tensor-level helper -----------------------------------------------------
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def gemm(A: torch.Tensor, B: torch.Tensor, bias: torch.Tensor | None = None, epilogue: str = "none",
+         b_col_major: bool = False, alpha: float = 1.0, out: torch.Tensor | None = None, config_id: int = -1,
+         stream: int | None = None) -> torch.Tensor:
+    """C = epilogue(alpha * A @ B + bias) on the GPU through tg_gemm_ex.
+
+    A: (M, K); B: (K, N), or (N, K) when b_col_major; bias: (N,) for the bias
+    epilogues.  fp16 or bf16, contiguous, on one HIP device.  The result has
+    the input dtype, or fp32 for ``epilogue="softmax"``.
+    """
+    if epilogue not in EPILOGUES:
+        raise ValueError(f"unknown epilogue {epilogue!r}")
+    epi = EPILOGUES[epilogue]
+    if A.dtype not in DTYPES or B.dtype != A.dtype or (bias is not None and bias.dtype != A.dtype):
+        raise TypeError("A, B and bias must share one dtype, float16 or bfloat16")
+    if not (A.is_cuda and B.is_cuda and (bias is None or bias.is_cuda)):
+        raise ValueError("tensors must be on a GPU")
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    M, K = A.shape
+    if b_col_major:
+        N, Kb = B.shape
+    else:
+        Kb, N = B.shape
+    if Kb != K:
+        raise ValueError(f"inner dimensions differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+    if bias is not None and (bias.dim() != 1 or bias.shape[0] != N):
+        raise ValueError("bias must have shape (N,)")
+    for name, t in (("A", A), ("B", B), ("bias", bias)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    out_dtype = torch.float32 if epi == TG_EPI_SOFTMAX else A.dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    elif out.shape != (M, N) or out.dtype != out_dtype or not out.is_contiguous() or out.device != A.device:
+        raise ValueError("out has the wrong shape, dtype, layout or device")
+    args = tg_gemm_args(A.data_ptr(), B.data_ptr(), bias.data_ptr() if bias is not None else None, out.data_ptr(),
+                        M, N, K, DTYPES[A.dtype], epi, int(bool(b_col_major)), float(alpha), int(config_id))
+    rc = tg_gemm_ex(args, stream if stream is not None else _stream_handle(A.device))
+    if rc != TG_OK:
+        raise TgError(rc, "tg_gemm_ex")
+    return out
+
+
+def query_config(M: int, N: int, K: int, dtype: torch.dtype, epilogue: str, b_col_major: bool = False) -> dict:
+    rc, cfg = tg_gemm_query_config(M, N, K, DTYPES[dtype], EPILOGUES[epilogue], int(bool(b_col_major)))
+    if rc != TG_OK:
+        raise TgError(rc, "tg_gemm_query_config")
+    return cfg.as_dict()
+
+
+def configs() -> list[dict]:
+    out = []
+    for i in range(tg_num_configs()):
+        rc, cfg = tg_get_config(i)
+        if rc != TG_OK:
+            raise TgError(rc, "tg_get_config")
+        out.append(cfg.as_dict())
+    return out

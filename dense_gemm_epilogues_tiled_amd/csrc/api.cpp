@@ -1,0 +1,233 @@
+// api.cpp -- the C ABI of include/tg.h: argument validation, tile
+// configuration lookup and kernel launch.
+//
+// The per-shape configuration choice mirrors the TileLang pages' autotuning
+// (noticiai.com.br, section "Exploracao de schedules com autotuning": a search
+// over tile sizes and warp counts keyed on (M, N, K), cached; spaxe.top,
+// autotuning paragraph): here the search runs offline (sweep.py) and its
+// winners are baked into config_table.inc; shapes without an entry fall back
+// to a rule that keeps every compute unit busy with the largest tile.
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "../../include/tg.h"
+#include "kernels.hpp"
+
+namespace tg {
+namespace {
+
+// Compute units of an MI355X; the fallback rule aims for at least one tile per CU.
+constexpr int kNumCUs = 256;
+
+// Descriptions of the compiled variants, in the order of gemm_launchers()
+// (gemm.hip) followed by softmax_launchers() (softmax.hip).
+//  id kind bm  bn  bk st waves mfma      wm wn gm xcd lds                 bcol
+const tg_tile_config kVariants[] = {
+    {0, TG_KERNEL_GEMM, 128, 128, 64, 2, 4, 16, 16, 32, 2, 2, 4, 1, 2 * (128 + 128) * 64 * 2, -1},
+    {1, TG_KERNEL_GEMM, 256, 128, 64, 2, 4, 16, 16, 32, 2, 2, 4, 1, 2 * (256 + 128) * 64 * 2, -1},
+    {2, TG_KERNEL_GEMM, 256, 256, 64, 2, 8, 16, 16, 32, 2, 4, 4, 1, 2 * (256 + 256) * 64 * 2, -1},
+    {3, TG_KERNEL_GEMM, 128, 64, 64, 2, 2, 16, 16, 32, 2, 1, 4, 1, 2 * (128 + 64) * 64 * 2, -1},
+    // softmax: bm = 16 rows, bn = widest row (waves * max tiles * 16), bk = 32 (one MFMA step)
+    {4, TG_KERNEL_GEMM_SOFTMAX, 16, 1024, 32, 2, 4, 16, 16, 32, 1, 4, 1, 0, 2 * 4 * 16 * 4, -1},
+    {5, TG_KERNEL_GEMM_SOFTMAX, 16, 2048, 32, 2, 8, 16, 16, 32, 1, 8, 1, 0, 2 * 8 * 16 * 4, -1},
+    {6, TG_KERNEL_GEMM_SOFTMAX, 16, 1024, 32, 2, 8, 16, 16, 32, 1, 8, 1, 0, 2 * 8 * 16 * 4, -1},
+};
+constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+constexpr int kFirstSoftmax = 4;
+
+// Baked per-shape choices written by the offline sweep.
+struct TableEntry {
+  int dtype, b_col_major, epilogue_kind;  // epilogue_kind: 0 elementwise, 1 softmax
+  int64_t M, N, K;
+  int variant, group_m, xcd_remap;
+};
+#include "config_table.inc"
+constexpr int kNumTable = sizeof(kTable) / sizeof(kTable[0]);
+
+bool log_enabled() {
+  const char* v = getenv("TG_LOG");
+  return v && v[0] && v[0] != '0';
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Choice {
+  int variant;
+  int group_m;
+  int xcd_remap;
+};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shape checks shared by the launch and the query (no pointers involved).
+int check_shape(int64_t M, int64_t N, int64_t K, int dtype, int epilogue, int b_col_major) {
+  if (dtype != TG_DTYPE_F16 && dtype != TG_DTYPE_BF16) return TG_ERR_INVALID_ARG;
+  if (epilogue < TG_EPI_NONE || epilogue > TG_EPI_SOFTMAX) return TG_ERR_INVALID_ARG;
+  if (b_col_major != 0 && b_col_major != 1) return TG_ERR_INVALID_ARG;
+  if (M < 0 || N < 0 || K < 0) return TG_ERR_INVALID_ARG;
+  if (M >= (int64_t(1) << 31) || N > (int64_t(1) << 24) || K > (int64_t(1) << 20)) return TG_ERR_UNSUPPORTED;
+  if (epilogue == TG_EPI_SOFTMAX && N > TG_SOFTMAX_MAX_N) return TG_ERR_UNSUPPORTED;
+  if ((N & 7) != 0 || (K & 7) != 0) return TG_ERR_MISALIGNED;
+  return TG_OK;
+}
+
+int softmax_capacity(const tg_tile_config& v) { return v.bn; }
+
+// Lookup: baked entry for the exact shape, else the fallback rule.
+Choice choose(int64_t M, int64_t N, int64_t K, int dtype, int epilogue, int b_col_major) {
+  const int kind = epilogue == TG_EPI_SOFTMAX ? 1 : 0;
+  for (int i = 0; i < kNumTable; ++i) {
+    const TableEntry& e = kTable[i];
+    if (e.dtype == dtype && e.b_col_major == b_col_major && e.epilogue_kind == kind && e.M == M && e.N == N &&
+        e.K == K)
+      return {e.variant, e.group_m, e.xcd_remap};
+  }
+  if (kind == 1) {
+    // the narrowest workgroup whose row capacity covers N
+    return {N <= 1024 ? 4 : 5, 1, 0};
+  }
+  // largest tile that still gives every CU a tile; else the smallest tile
+  static const int order[] = {2, 1, 0, 3};
+  for (int v : order) {
+    const int64_t tiles = cdiv(M, kVariants[v].bm) * cdiv(N, kVariants[v].bn);
+    if (tiles >= kNumCUs) return {v, kVariants[v].group_m, 1};
+  }
+  return {3, kVariants[3].group_m, 1};
+}
+
+}  // namespace
+}  // namespace tg
+
+using namespace tg;
+
+extern "C" {
+
+int tg_version(void) { return TG_VERSION_MAJOR * 100 + TG_VERSION_MINOR; }
+
+const char* tg_status_string(int status) {
+  switch (status) {
+    case TG_OK: return "TG_OK: success";
+    case TG_ERR_INVALID_ARG: return "TG_ERR_INVALID_ARG: invalid argument";
+    case TG_ERR_UNSUPPORTED: return "TG_ERR_UNSUPPORTED: request outside the implemented kernels";
+    case TG_ERR_MISALIGNED: return "TG_ERR_MISALIGNED: pointer not 16-byte aligned or N/K not a multiple of 8";
+    case TG_ERR_HIP: return "TG_ERR_HIP: the HIP runtime rejected the launch";
+    default: return "unknown tg status";
+  }
+}
+
+int tg_num_configs(void) { return kNumVariants; }
+
+int tg_get_config(int index, tg_tile_config* out) {
+  if (!out || index < 0 || index >= kNumVariants) return TG_ERR_INVALID_ARG;
+  *out = kVariants[index];
+  return TG_OK;
+}
+
+int tg_gemm_query_config(int64_t M, int64_t N, int64_t K, int dtype, int epilogue, int b_col_major,
+                         tg_tile_config* out) {
+  if (!out) return TG_ERR_INVALID_ARG;
+  const int rc = check_shape(M, N, K, dtype, epilogue, b_col_major);
+  if (rc != TG_OK) return rc;
+  const Choice c = choose(M, N, K, dtype, epilogue, b_col_major);
+  *out = kVariants[c.variant];
+  out->group_m = c.group_m;
+  out->xcd_remap = c.xcd_remap;
+  out->b_col_major = b_col_major;
+  return TG_OK;
+}
+
+int tg_gemm_ex(const tg_gemm_args* a, void* stream) {
+  if (!a) return TG_ERR_INVALID_ARG;
+  int rc = check_shape(a->M, a->N, a->K, a->dtype, a->epilogue, a->b_col_major);
+  if (rc != TG_OK) return rc;
+  const bool wants_bias = a->epilogue == TG_EPI_BIAS || a->epilogue == TG_EPI_BIAS_RELU ||
+                          a->epilogue == TG_EPI_BIAS_GELU;
+  if (wants_bias != (a->bias != nullptr)) return TG_ERR_INVALID_ARG;
+  const int kind = a->epilogue == TG_EPI_SOFTMAX ? TG_KERNEL_GEMM_SOFTMAX : TG_KERNEL_GEMM;
+
+  Choice c;
+  if (a->config_id >= 0) {
+    if (a->config_id >= kNumVariants || kVariants[a->config_id].kind != kind) return TG_ERR_INVALID_ARG;
+    c = {a->config_id, kVariants[a->config_id].group_m, kVariants[a->config_id].xcd_remap};
+    if (kind == TG_KERNEL_GEMM_SOFTMAX && a->N > softmax_capacity(kVariants[a->config_id]))
+      return TG_ERR_UNSUPPORTED;
+  } else {
+    c = choose(a->M, a->N, a->K, a->dtype, a->epilogue, a->b_col_major);
+  }
+
+  if (a->M == 0 || a->N == 0) return TG_OK;  // empty output: nothing to launch
+  if (!a->C || (a->K > 0 && (!a->A || !a->B))) return TG_ERR_INVALID_ARG;
+  if (!aligned16(a->C) || (a->K > 0 && (!aligned16(a->A) || !aligned16(a->B))) ||
+      (a->bias && !aligned16(a->bias)))
+    return TG_ERR_MISALIGNED;
+
+  const tg_tile_config& v = kVariants[c.variant];
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  int grid = 0;
+  if (kind == TG_KERNEL_GEMM) {
+    GemmParams p;
+    p.A = a->A;
+    p.B = a->B;
+    p.bias = a->bias;
+    p.C = a->C;
+    p.M = (int)a->M;
+    p.N = (int)a->N;
+    p.K = (int)a->K;
+    p.alpha = a->alpha;
+    p.epilogue = a->epilogue;
+    p.tiles_m = (int)cdiv(a->M, v.bm);
+    p.tiles_n = (int)cdiv(a->N, v.bn);
+    p.group_m = c.group_m > 0 ? c.group_m : 1;
+    p.xcd_remap = c.xcd_remap;
+    if ((int64_t)p.tiles_m * p.tiles_n >= (int64_t(1) << 31)) return TG_ERR_UNSUPPORTED;
+    grid = p.tiles_m * p.tiles_n;
+    int n_l = 0;
+    const GemmLauncherSet* L = gemm_launchers(&n_l);
+    if (c.variant >= n_l) return TG_ERR_INVALID_ARG;
+    err = L[c.variant].fn[a->dtype][a->b_col_major](p, s);
+  } else {
+    SoftmaxParams p;
+    p.A = a->A;
+    p.B = a->B;
+    p.C = static_cast<float*>(a->C);
+    p.M = (int)a->M;
+    p.N = (int)a->N;
+    p.K = (int)a->K;
+    p.alpha = a->alpha;
+    p.n_sub = (int)cdiv(a->N, 16 * v.waves);
+    grid = (int)cdiv(a->M, 16);
+    int n_l = 0;
+    const SoftmaxLauncherSet* L = softmax_launchers(&n_l);
+    if (c.variant - kFirstSoftmax >= n_l) return TG_ERR_INVALID_ARG;
+    err = L[c.variant - kFirstSoftmax].fn[a->dtype][a->b_col_major](p, s);
+  }
+  if (log_enabled())
+    fprintf(stderr, "tg: M=%lld N=%lld K=%lld dtype=%d epi=%d bcol=%d cfg=%d (%dx%d) grid=%d group_m=%d xcd=%d -> %s\n",
+            (long long)a->M, (long long)a->N, (long long)a->K, a->dtype, a->epilogue, a->b_col_major, c.variant, v.bm,
+            v.bn, grid, c.group_m, c.xcd_remap, hipGetErrorString(err));
+  return err == hipSuccess ? TG_OK : TG_ERR_HIP;
+}
+
+int tg_gemm(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N, int64_t K, int dtype,
+            int epilogue, void* stream) {
+  tg_gemm_args a;
+  a.A = A;
+  a.B = B;
+  a.bias = bias;
+  a.C = C;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.dtype = dtype;
+  a.epilogue = epilogue;
+  a.b_col_major = 0;
+  a.alpha = 1.0f;
+  a.config_id = -1;
+  return tg_gemm_ex(&a, stream);
+}
+
+}  // extern "C"

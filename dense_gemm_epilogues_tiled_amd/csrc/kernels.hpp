@@ -1,0 +1,53 @@
+// kernels.hpp -- interface between the host dispatch (api.cpp) and the
+// compiled kernel variants (gemm.hip, softmax.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tg.h"
+
+namespace tg {
+
+// Kernel arguments of the 2-D tiled GEMM (sizes already validated on the host
+// to fit the kernels' 32-bit offsets).
+struct GemmParams {
+  const void* A;
+  const void* B;
+  const void* bias;
+  void* C;
+  int M, N, K;
+  float alpha;
+  int epilogue;
+  int tiles_m, tiles_n;
+  int group_m;
+  int xcd_remap;
+};
+
+// Kernel arguments of the full-row GEMM + row softmax.
+struct SoftmaxParams {
+  const void* A;
+  const void* B;
+  float* C;
+  int M, N, K;
+  float alpha;
+  int n_sub;  // 16-column MFMA tiles per wave: ceil(N / (16 * waves))
+};
+
+typedef hipError_t (*GemmLaunchFn)(const GemmParams&, hipStream_t);
+typedef hipError_t (*SoftmaxLaunchFn)(const SoftmaxParams&, hipStream_t);
+
+// Launchers of one GEMM tile shape: [dtype][b_col_major].
+struct GemmLauncherSet {
+  GemmLaunchFn fn[2][2];
+};
+// Launchers of one softmax shape: [dtype][b_col_major].
+struct SoftmaxLauncherSet {
+  SoftmaxLaunchFn fn[2][2];
+};
+
+// Launcher tables of the compiled variants (defined next to the kernels).
+const GemmLauncherSet* gemm_launchers(int* count);
+const SoftmaxLauncherSet* softmax_launchers(int* count);
+
+}  // namespace tg

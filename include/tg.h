@@ -1,0 +1,180 @@
+/*
+ * tg.h -- C ABI of the MI355X (gfx950) fused-epilogue tiled GEMM library.
+ *
+ *     C = epilogue(alpha * A.B + bias)
+ *
+ * The operation is the one the TileLang tutorial pages build up to:
+ *   - "TileLang: Criando Kernels de GPU de Alto Desempenho com Tensor Cores,
+ *     FlashAttention e Autotuning" (noticiai.com.br): section "GEMM com Tensor
+ *     Cores" (tiled product on the matrix units), section "GEMM com epilogo
+ *     fundido" (ReLU, bias and GELU applied to the accumulator inside the same
+ *     kernel, no round trip to DRAM), section "Exploracao de schedules com
+ *     autotuning" (a tile configuration chosen per matrix shape);
+ *   - the edgex.exchange page on the TileLang Python DSL, paragraph on the
+ *     fused epilogue (bias and GELU applied to the register-resident
+ *     accumulator before the single write of the output);
+ *   - "Designing High-Performance GPU Kernels with TileLang ..." (spaxe.top),
+ *     paragraph on the row softmax applied in the GEMM epilogue without
+ *     writing the intermediate product to global memory.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Layout   A is M x K row-major (K contiguous).  B is K x N row-major by
+ *           default; with b_col_major = 1 it is stored N x K row-major (the
+ *           "key" matrix of an attention-score product).  C is M x N
+ *           row-major.  Leading dimensions are packed (lda = K, ldb = N or K,
+ *           ldc = N).
+ *  Types    TG_DTYPE_F16: A, B, bias and C are IEEE binary16.
+ *           TG_DTYPE_BF16: A, B, bias and C are bfloat16.
+ *           TG_EPI_SOFTMAX writes C as fp32 whatever the input dtype.
+ *           Products are accumulated in fp32 on the matrix cores; the
+ *           epilogue runs in fp32 and the result is rounded once, to nearest
+ *           even, to the output type.
+ *  Math     x_ij = alpha * sum_k A_ik B_kj + bias_j   (bias broadcast over rows)
+ *           TG_EPI_NONE       C = x          (bias must be NULL)
+ *           TG_EPI_BIAS       C = x
+ *           TG_EPI_BIAS_RELU  C = max(x, 0)
+ *           TG_EPI_BIAS_GELU  C = x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2))
+ *           TG_EPI_SOFTMAX    C_ij = exp(x_ij - max_j x_ij) / sum_j exp(...)
+ *                             (bias must be NULL; row length N <= TG_SOFTMAX_MAX_N)
+ *  Memory   Every pointer is a device pointer owned by the caller.  The library
+ *           never allocates, frees or synchronises; it only enqueues one kernel
+ *           on `stream` (a hipStream_t; NULL = the null stream).  It keeps no
+ *           mutable state, so concurrent calls from several host threads are
+ *           safe.  C must not overlap A, B or bias.
+ *  Errors   Every entry point returns a tg_status.  All argument checks run on
+ *           the host before any HIP call, so an invalid call touches no device
+ *           and enqueues nothing.  A launch failure reported by the runtime
+ *           returns TG_ERR_HIP.  Faults during kernel execution surface at the
+ *           caller's next synchronisation.  Nothing throws, aborts or prints
+ *           (set TG_LOG=1 in the environment to log each launch to stderr).
+ *  Limits   0 <= M < 2^31, 0 <= N <= 2^24, 0 <= K <= 2^20 (the kernels use
+ *           32-bit offsets inside a tile); N and K multiples of 8 (16-byte
+ *           rows); A, B, bias and C 16-byte aligned.  Negative sizes return
+ *           TG_ERR_INVALID_ARG, larger sizes TG_ERR_UNSUPPORTED, alignment
+ *           violations TG_ERR_MISALIGNED.
+ *  Degenerate  M == 0 or N == 0: nothing is launched, TG_OK.
+ *           K == 0: the product is zero and C = epilogue(bias).
+ */
+#ifndef TG_H_
+#define TG_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TG_VERSION_MAJOR 0
+#define TG_VERSION_MINOR 1
+
+/* Longest softmax row the on-chip row kernel holds (fp32 values per row). */
+#define TG_SOFTMAX_MAX_N 2048
+
+typedef enum tg_status {
+  TG_OK = 0,
+  TG_ERR_INVALID_ARG = -1, /* NULL pointer, negative size, unknown enum, bad config id */
+  TG_ERR_UNSUPPORTED = -2, /* valid request outside what the kernels implement */
+  TG_ERR_MISALIGNED = -3,  /* pointer not 16-byte aligned, or N / K not a multiple of 8 */
+  TG_ERR_HIP = -4          /* the HIP runtime rejected the launch */
+} tg_status;
+
+typedef enum tg_dtype { TG_DTYPE_F16 = 0, TG_DTYPE_BF16 = 1 } tg_dtype;
+
+typedef enum tg_epilogue {
+  TG_EPI_NONE = 0,
+  TG_EPI_BIAS = 1,
+  TG_EPI_BIAS_RELU = 2,
+  TG_EPI_BIAS_GELU = 3,
+  TG_EPI_SOFTMAX = 4
+} tg_epilogue;
+
+/* Kernel families a tile configuration belongs to. */
+typedef enum tg_kernel_kind {
+  TG_KERNEL_GEMM = 0,        /* 2-D output tiles, elementwise epilogues */
+  TG_KERNEL_GEMM_SOFTMAX = 1 /* full-row tiles, row softmax epilogue */
+} tg_kernel_kind;
+
+/*
+ * One compiled tile configuration (read-only; describes a kernel variant).
+ * bm x bn output tile per workgroup, bk-deep K steps, `stages` LDS buffers,
+ * waves = wave_m * wave_n 64-lane wavefronts per workgroup, MFMA shape
+ * mfma_m x mfma_n x mfma_k, group_m = tile rows per L2 raster band,
+ * xcd_remap = 1 when workgroups are regrouped so each XCD owns a contiguous
+ * block of tiles, lds_bytes = LDS per workgroup, b_col_major = the B layout
+ * the variant is compiled for (-1: any).
+ */
+typedef struct tg_tile_config {
+  int32_t id;
+  int32_t kind;
+  int32_t bm, bn, bk;
+  int32_t stages;
+  int32_t waves;
+  int32_t mfma_m, mfma_n, mfma_k;
+  int32_t wave_m, wave_n;
+  int32_t group_m;
+  int32_t xcd_remap;
+  int32_t lds_bytes;
+  int32_t b_col_major;
+} tg_tile_config;
+
+/* Full argument block of tg_gemm_ex.  config_id < 0 selects from the built-in
+ * table; config_id >= 0 forces that compiled configuration (it must be of the
+ * right kind and B layout, else TG_ERR_INVALID_ARG). */
+typedef struct tg_gemm_args {
+  const void* A;
+  const void* B;
+  const void* bias;
+  void* C;
+  int64_t M, N, K;
+  int32_t dtype;
+  int32_t epilogue;
+  int32_t b_col_major;
+  float alpha;
+  int32_t config_id;
+} tg_gemm_args;
+
+/*
+ * tg_gemm -- C = epilogue(A.B + bias) with alpha = 1 and B row-major (K x N).
+ * A: M x K, B: K x N, bias: N elements (required for TG_EPI_BIAS*, must be NULL
+ * otherwise), C: M x N (fp32 for TG_EPI_SOFTMAX, else the input dtype).
+ * stream: hipStream_t to enqueue on.  Returns TG_OK or an error code (above).
+ */
+int tg_gemm(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N, int64_t K,
+            int dtype, int epilogue, void* stream);
+
+/*
+ * tg_gemm_ex -- the general form: adds alpha (scales the fp32 accumulator
+ * before the bias), the B layout flag and an optional forced configuration.
+ * The row-softmax workload (attention scores Q.K^T / sqrt(d)) is a call with
+ * b_col_major = 1 and alpha = 1/sqrt(d).  args must not be NULL.
+ */
+int tg_gemm_ex(const tg_gemm_args* args, void* stream);
+
+/*
+ * tg_gemm_query_config -- the configuration tg_gemm / tg_gemm_ex would launch
+ * for this problem (the same lookup, no launch, no HIP call).  Writes *out.
+ * Returns TG_OK, TG_ERR_INVALID_ARG (NULL out, bad enums, negative sizes) or
+ * TG_ERR_UNSUPPORTED (e.g. softmax row longer than TG_SOFTMAX_MAX_N).
+ */
+int tg_gemm_query_config(int64_t M, int64_t N, int64_t K, int dtype, int epilogue, int b_col_major,
+                         tg_tile_config* out);
+
+/* Number of compiled tile configurations (ids 0 .. n-1). */
+int tg_num_configs(void);
+
+/* Describe compiled configuration `index`; TG_ERR_INVALID_ARG if out of range
+ * or out is NULL. */
+int tg_get_config(int index, tg_tile_config* out);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* tg_status_string(int status);
+
+/* Library version as major * 100 + minor. */
+int tg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TG_H_ */

@@ -1,0 +1,75 @@
+"""Comparison helpers for GPU-vs-oracle tests (no method arithmetic here).
+
+Acceptance (per output element g against the oracle's fp64 value y):
+    |g - y| <= 1e-2 + 1e-2 |y|   for fp16 / bf16 outputs,
+    |g - y| <= 1e-4 + 1e-4 |y|   for the fp32 softmax output,
+and ||g - y||_F / ||y||_F <= 2e-3 over the compared set, with no NaN or Inf.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+TOL = {"f16": (1e-2, 1e-2), "bf16": (1e-2, 1e-2), "f32": (1e-4, 1e-4)}
+FROB = 2e-3
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def stats(g: np.ndarray, y: np.ndarray, out_dtype: str) -> dict:
+    atol, rtol = TOL[out_dtype]
+    err = np.abs(g - y)
+    bound = atol + rtol * np.abs(y)
+    ny = np.linalg.norm(y.ravel())
+    return {
+        "finite": bool(np.all(np.isfinite(g))),
+        "n": int(g.size),
+        "n_fail": int(np.sum(~(err <= bound))),
+        "max_abs": float(err.max()) if g.size else 0.0,
+        "frob_rel": float(np.linalg.norm((g - y).ravel()) / ny) if ny > 0 else float(np.linalg.norm(g.ravel())),
+    }
+
+
+def assert_accept(g: np.ndarray, y: np.ndarray, out_dtype: str, what: str = "") -> dict:
+    s = stats(g, y, out_dtype)
+    assert s["finite"], f"{what}: NaN/Inf in GPU output"
+    assert s["n_fail"] == 0, f"{what}: {s['n_fail']} of {s['n']} elements outside tolerance, {s}"
+    assert s["frob_rel"] <= FROB, f"{what}: relative Frobenius error {s['frob_rel']:.3e} > {FROB}"
+    return s
+
+
+# ---- rounding of fp64 reference values to the output format -----------------
+
+def rne_f16_bits(y: np.ndarray) -> np.ndarray:
+    """Round fp64 -> binary16, nearest even (numpy converts double -> half directly)."""
+    return y.astype(np.float16).view(np.uint16)
+
+
+def rne_bf16_bits(y: np.ndarray) -> np.ndarray:
+    """Round fp64 -> bfloat16 (8-bit significand), nearest even, for normal-range values."""
+    y = np.asarray(y, dtype=np.float64)
+    out = np.zeros(y.shape, dtype=np.float64)
+    nz = y != 0
+    e = np.floor(np.log2(np.abs(y[nz])))
+    # guard log2 rounding at exact powers of two
+    e = np.where(np.abs(y[nz]) < 2.0 ** e, e - 1, e)
+    e = np.where(np.abs(y[nz]) >= 2.0 ** (e + 1), e + 1, e)
+    ulp = 2.0 ** (e - 7)
+    out[nz] = np.round(y[nz] / ulp) * ulp  # exact division by a power of two; np.round ties to even
+    f32 = out.astype(np.float32)           # exact: the value has 8 significant bits
+    return (f32.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def ulp_distance(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """Distance in units in the last place between 16-bit sign-magnitude floats."""
+    def ordered(b):
+        b = b.astype(np.int32)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
