@@ -65,7 +65,8 @@ class tg_gemm_args(ctypes.Structure):
         ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("C", ctypes.c_void_p),
         ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
         ("dtype", ctypes.c_int32), ("epilogue", ctypes.c_int32), ("b_col_major", ctypes.c_int32),
-        ("alpha", ctypes.c_float), ("config_id", ctypes.c_int32),
+        ("alpha", ctypes.c_float), ("config_id", ctypes.c_int32), ("group_m", ctypes.c_int32),
+        ("xcd_remap", ctypes.c_int32),
     ]
 
 
@@ -155,7 +156,7 @@ def _stream_handle(device: torch.device) -> int:
 
 def gemm(A: torch.Tensor, B: torch.Tensor, bias: torch.Tensor | None = None, epilogue: str = "none",
          b_col_major: bool = False, alpha: float = 1.0, out: torch.Tensor | None = None, config_id: int = -1,
-         stream: int | None = None) -> torch.Tensor:
+         stream: int | None = None, group_m: int = 0, xcd_remap: int = -1) -> torch.Tensor:
     """C = epilogue(alpha * A @ B + bias) on the GPU through tg_gemm_ex.
 
     A: (M, K); B: (K, N), or (N, K) when b_col_major; bias: (N,) for the bias
@@ -189,7 +190,8 @@ def gemm(A: torch.Tensor, B: torch.Tensor, bias: torch.Tensor | None = None, epi
     elif out.shape != (M, N) or out.dtype != out_dtype or not out.is_contiguous() or out.device != A.device:
         raise ValueError("out has the wrong shape, dtype, layout or device")
     args = tg_gemm_args(A.data_ptr(), B.data_ptr(), bias.data_ptr() if bias is not None else None, out.data_ptr(),
-                        M, N, K, DTYPES[A.dtype], epi, int(bool(b_col_major)), float(alpha), int(config_id))
+                        M, N, K, DTYPES[A.dtype], epi, int(bool(b_col_major)), float(alpha), int(config_id),
+                        int(group_m), int(xcd_remap))
     rc = tg_gemm_ex(args, stream if stream is not None else _stream_handle(A.device))
     if rc != TG_OK:
         raise TgError(rc, "tg_gemm_ex")

@@ -22,21 +22,29 @@ namespace {
 // Compute units of an MI355X; the fallback rule aims for at least one tile per CU.
 constexpr int kNumCUs = 256;
 
-// Descriptions of the compiled variants, in the order of gemm_launchers()
-// (gemm.hip) followed by softmax_launchers() (softmax.hip).
-//  id kind bm  bn  bk st waves mfma      wm wn gm xcd lds                 bcol
-const tg_tile_config kVariants[] = {
-    {0, TG_KERNEL_GEMM, 128, 128, 64, 2, 4, 16, 16, 32, 2, 2, 4, 1, 2 * (128 + 128) * 64 * 2, -1},
-    {1, TG_KERNEL_GEMM, 256, 128, 64, 2, 4, 16, 16, 32, 2, 2, 4, 1, 2 * (256 + 128) * 64 * 2, -1},
-    {2, TG_KERNEL_GEMM, 256, 256, 64, 2, 8, 16, 16, 32, 2, 4, 4, 1, 2 * (256 + 256) * 64 * 2, -1},
-    {3, TG_KERNEL_GEMM, 128, 64, 64, 2, 2, 16, 16, 32, 2, 1, 4, 1, 2 * (128 + 64) * 64 * 2, -1},
-    // softmax: bm = 16 rows, bn = widest row (waves * max tiles * 16), bk = 32 (one MFMA step)
-    {4, TG_KERNEL_GEMM_SOFTMAX, 16, 1024, 32, 2, 4, 16, 16, 32, 1, 4, 1, 0, 2 * 4 * 16 * 4, -1},
-    {5, TG_KERNEL_GEMM_SOFTMAX, 16, 2048, 32, 2, 8, 16, 16, 32, 1, 8, 1, 0, 2 * 8 * 16 * 4, -1},
-    {6, TG_KERNEL_GEMM_SOFTMAX, 16, 1024, 32, 2, 8, 16, 16, 32, 1, 8, 1, 0, 2 * 8 * 16 * 4, -1},
+// All compiled configurations: the GEMM variants (gemm.hip) with ids
+// 0 .. G-1, then the row-softmax variants (softmax.hip) with ids G ...
+struct Registry {
+  const GemmVariant* gemm;
+  const SoftmaxVariant* softmax;
+  int n_gemm, n_softmax;
+  tg_tile_config cfg[64];
+  int n;
 };
-constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
-constexpr int kFirstSoftmax = 4;
+
+const Registry& registry() {
+  static const Registry r = [] {
+    Registry x{};
+    x.gemm = gemm_variants(&x.n_gemm);
+    x.softmax = softmax_variants(&x.n_softmax);
+    x.n = 0;
+    for (int i = 0; i < x.n_gemm && x.n < 64; ++i) x.cfg[x.n++] = x.gemm[i].cfg;
+    for (int i = 0; i < x.n_softmax && x.n < 64; ++i) x.cfg[x.n++] = x.softmax[i].cfg;
+    for (int i = 0; i < x.n; ++i) x.cfg[i].id = i;
+    return x;
+  }();
+  return r;
+}
 
 // Baked per-shape choices written by the offline sweep.
 struct TableEntry {
@@ -76,26 +84,41 @@ int check_shape(int64_t M, int64_t N, int64_t K, int dtype, int epilogue, int b_
 
 int softmax_capacity(const tg_tile_config& v) { return v.bn; }
 
+int64_t tiles_of(const tg_tile_config& c, int64_t M, int64_t N) { return cdiv(M, c.bm) * cdiv(N, c.bn); }
+
 // Lookup: baked entry for the exact shape, else the fallback rule.
 Choice choose(int64_t M, int64_t N, int64_t K, int dtype, int epilogue, int b_col_major) {
+  const Registry& R = registry();
   const int kind = epilogue == TG_EPI_SOFTMAX ? 1 : 0;
   for (int i = 0; i < kNumTable; ++i) {
     const TableEntry& e = kTable[i];
     if (e.dtype == dtype && e.b_col_major == b_col_major && e.epilogue_kind == kind && e.M == M && e.N == N &&
-        e.K == K)
+        e.K == K && e.variant >= 0 && e.variant < R.n && R.cfg[e.variant].kind == kind)
       return {e.variant, e.group_m, e.xcd_remap};
   }
   if (kind == 1) {
-    // the narrowest workgroup whose row capacity covers N
-    return {N <= 1024 ? 4 : 5, 1, 0};
+    // the softmax variant with the fewest waves whose row capacity covers N
+    int best = -1;
+    for (int i = R.n_gemm; i < R.n; ++i)
+      if (R.cfg[i].bn >= N && (best < 0 || R.cfg[i].waves < R.cfg[best].waves)) best = i;
+    return {best, 1, 0};
   }
-  // largest tile that still gives every CU a tile; else the smallest tile
-  static const int order[] = {2, 1, 0, 3};
-  for (int v : order) {
-    const int64_t tiles = cdiv(M, kVariants[v].bm) * cdiv(N, kVariants[v].bn);
-    if (tiles >= kNumCUs) return {v, kVariants[v].group_m, 1};
+  // the largest tile that still gives every CU at least one tile; failing
+  // that (small problems), the variant with the most tiles
+  int best = -1;
+  for (int i = 0; i < R.n_gemm; ++i) {
+    const tg_tile_config& c = R.cfg[i];
+    if (tiles_of(c, M, N) < kNumCUs) continue;
+    if (best < 0 || c.bm * c.bn > R.cfg[best].bm * R.cfg[best].bn ||
+        (c.bm * c.bn == R.cfg[best].bm * R.cfg[best].bn && c.bk > R.cfg[best].bk))
+      best = i;
   }
-  return {3, kVariants[3].group_m, 1};
+  if (best < 0) {
+    best = 0;
+    for (int i = 1; i < R.n_gemm; ++i)
+      if (tiles_of(R.cfg[i], M, N) > tiles_of(R.cfg[best], M, N)) best = i;
+  }
+  return {best, R.cfg[best].group_m, R.cfg[best].xcd_remap};
 }
 
 }  // namespace
@@ -118,11 +141,11 @@ const char* tg_status_string(int status) {
   }
 }
 
-int tg_num_configs(void) { return kNumVariants; }
+int tg_num_configs(void) { return registry().n; }
 
 int tg_get_config(int index, tg_tile_config* out) {
-  if (!out || index < 0 || index >= kNumVariants) return TG_ERR_INVALID_ARG;
-  *out = kVariants[index];
+  if (!out || index < 0 || index >= registry().n) return TG_ERR_INVALID_ARG;
+  *out = registry().cfg[index];
   return TG_OK;
 }
 
@@ -132,7 +155,8 @@ int tg_gemm_query_config(int64_t M, int64_t N, int64_t K, int dtype, int epilogu
   const int rc = check_shape(M, N, K, dtype, epilogue, b_col_major);
   if (rc != TG_OK) return rc;
   const Choice c = choose(M, N, K, dtype, epilogue, b_col_major);
-  *out = kVariants[c.variant];
+  if (c.variant < 0) return TG_ERR_UNSUPPORTED;
+  *out = registry().cfg[c.variant];
   out->group_m = c.group_m;
   out->xcd_remap = c.xcd_remap;
   out->b_col_major = b_col_major;
@@ -148,15 +172,19 @@ int tg_gemm_ex(const tg_gemm_args* a, void* stream) {
   if (wants_bias != (a->bias != nullptr)) return TG_ERR_INVALID_ARG;
   const int kind = a->epilogue == TG_EPI_SOFTMAX ? TG_KERNEL_GEMM_SOFTMAX : TG_KERNEL_GEMM;
 
+  const Registry& R = registry();
   Choice c;
   if (a->config_id >= 0) {
-    if (a->config_id >= kNumVariants || kVariants[a->config_id].kind != kind) return TG_ERR_INVALID_ARG;
-    c = {a->config_id, kVariants[a->config_id].group_m, kVariants[a->config_id].xcd_remap};
-    if (kind == TG_KERNEL_GEMM_SOFTMAX && a->N > softmax_capacity(kVariants[a->config_id]))
-      return TG_ERR_UNSUPPORTED;
+    if (a->config_id >= R.n || R.cfg[a->config_id].kind != kind) return TG_ERR_INVALID_ARG;
+    c = {a->config_id, R.cfg[a->config_id].group_m, R.cfg[a->config_id].xcd_remap};
+    if (kind == TG_KERNEL_GEMM_SOFTMAX && a->N > softmax_capacity(R.cfg[a->config_id])) return TG_ERR_UNSUPPORTED;
   } else {
     c = choose(a->M, a->N, a->K, a->dtype, a->epilogue, a->b_col_major);
+    if (c.variant < 0) return TG_ERR_UNSUPPORTED;
   }
+  if (a->group_m < 0 || a->group_m > 4096 || a->xcd_remap < -1 || a->xcd_remap > 1) return TG_ERR_INVALID_ARG;
+  if (a->group_m > 0) c.group_m = a->group_m;
+  if (a->xcd_remap >= 0) c.xcd_remap = a->xcd_remap;
 
   if (a->M == 0 || a->N == 0) return TG_OK;  // empty output: nothing to launch
   if (!a->C || (a->K > 0 && (!a->A || !a->B))) return TG_ERR_INVALID_ARG;
@@ -164,7 +192,7 @@ int tg_gemm_ex(const tg_gemm_args* a, void* stream) {
       (a->bias && !aligned16(a->bias)))
     return TG_ERR_MISALIGNED;
 
-  const tg_tile_config& v = kVariants[c.variant];
+  const tg_tile_config& v = R.cfg[c.variant];
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
   int grid = 0;
@@ -185,10 +213,7 @@ int tg_gemm_ex(const tg_gemm_args* a, void* stream) {
     p.xcd_remap = c.xcd_remap;
     if ((int64_t)p.tiles_m * p.tiles_n >= (int64_t(1) << 31)) return TG_ERR_UNSUPPORTED;
     grid = p.tiles_m * p.tiles_n;
-    int n_l = 0;
-    const GemmLauncherSet* L = gemm_launchers(&n_l);
-    if (c.variant >= n_l) return TG_ERR_INVALID_ARG;
-    err = L[c.variant].fn[a->dtype][a->b_col_major](p, s);
+    err = R.gemm[c.variant].fn[a->dtype][a->b_col_major](p, s);
   } else {
     SoftmaxParams p;
     p.A = a->A;
@@ -200,10 +225,7 @@ int tg_gemm_ex(const tg_gemm_args* a, void* stream) {
     p.alpha = a->alpha;
     p.n_sub = (int)cdiv(a->N, 16 * v.waves);
     grid = (int)cdiv(a->M, 16);
-    int n_l = 0;
-    const SoftmaxLauncherSet* L = softmax_launchers(&n_l);
-    if (c.variant - kFirstSoftmax >= n_l) return TG_ERR_INVALID_ARG;
-    err = L[c.variant - kFirstSoftmax].fn[a->dtype][a->b_col_major](p, s);
+    err = R.softmax[c.variant - R.n_gemm].fn[a->dtype][a->b_col_major](p, s);
   }
   if (log_enabled())
     fprintf(stderr, "tg: M=%lld N=%lld K=%lld dtype=%d epi=%d bcol=%d cfg=%d (%dx%d) grid=%d group_m=%d xcd=%d -> %s\n",
@@ -227,6 +249,8 @@ int tg_gemm(const void* A, const void* B, const void* bias, void* C, int64_t M, 
   a.b_col_major = 0;
   a.alpha = 1.0f;
   a.config_id = -1;
+  a.group_m = 0;
+  a.xcd_remap = -1;
   return tg_gemm_ex(&a, stream);
 }
 

@@ -55,30 +55,79 @@ __device__ __forceinline__ f32x4 mfma16x16x32(BF16, const u32x4& a, const u32x4&
 }
 
 // ---------------------------------------------------------------------------
-// LDS tile layout for 64-element (128-byte) K rows.
+// LDS tile layouts.  LDS has 64 four-byte banks: one 256-byte window.
 //
-// A tile of R rows x 64 k (fp16/bf16) is stored as R/2 lines of 256 bytes,
-// two rows per line, in 16-byte slots.  Row r, 16-byte chunk c (k = 8c..8c+7)
-// lives in line r/2 at slot
-//     ((r & 1) ^ (line >> 2 & 1)) * 8 + (c ^ (line & 7)),   line = r / 2.
-// Fragment reads (16 consecutive rows, one chunk) hit 16 distinct slots, i.e.
-// all 64 banks once; row writes of 16-byte chunks are conflict-free too, and
-// the transposed 8-byte writes of row-major B spread over both halves.
+// K-contiguous tiles (A, and B stored N x K): R rows x BK k of 16-bit values,
+// row r at r * 2BK bytes, 16-byte chunk c (k = 8c .. 8c+7) stored in slot
+//     c ^ ((r / (16 / KCH)) % KCH),      KCH = BK / 8 chunks per row.
+// A fragment read touches 16 consecutive rows at one chunk; the XOR spreads
+// them over 16 distinct 16-byte slots of the 256-byte bank window.
+//
+// N-contiguous tiles (B stored K x N, BN >= 128): row k at k * 2BN bytes,
+// 16-byte chunk c (n = 8c .. 8c+7) stored in slot
+//     ((c / 2) ^ s(k)) * 2 + (c % 2),    s(k) = (k % 4) + 4 * ((k / 8) % 2).
+// ds_read_b64_tr_b16 fragment reads touch 8 rows x 32 bytes per half-wave;
+// the XOR puts those 8 pairs of chunks in distinct slots.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int lds_off64(int row, int chunk) {
-  const int line = row >> 1;
-  const int slot = ((((row & 1) ^ ((line >> 2) & 1))) << 3) | (chunk ^ (line & 7));
-  return (line << 8) | (slot << 4);
+template <int BK>
+__device__ __forceinline__ int kc_off(int row, int chunk) {
+  constexpr int KCH = BK / 8;
+  constexpr int R = 16 / KCH;
+  return row * (BK * 2) + 16 * (chunk ^ ((row / R) % KCH));
 }
+
+__device__ __forceinline__ int nc_swz(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
+
+template <int BN>
+__device__ __forceinline__ int nc_off(int k, int chunk) {
+  return k * (BN * 2) + 16 * ((((chunk >> 1) ^ nc_swz(k)) << 1) | (chunk & 1));
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 __device__ __forceinline__ u32x4 lds_read16(const unsigned char* base, int off) {
   return *reinterpret_cast<const u32x4*>(base + off);
 }
-__device__ __forceinline__ void lds_write16(unsigned char* base, int off, const u32x4& v) {
-  *reinterpret_cast<u32x4*>(base + off) = v;
+
+// Transposing LDS read (gfx950): within each 16-lane group, lane j supplies
+// the address of 4 consecutive 16-bit values; lane i receives element i % 4 of
+// lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4.  When lanes 4q .. 4q+3 point at the
+// four 8-byte pieces of a 16-wide row q, lane i ends with column i of rows 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr8(const unsigned char* base, int off) {
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  lds_u8* q = (lds_u8*)(unsigned char*)(base + off);  // generic -> LDS address space
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)q);
+  return __builtin_bit_cast(u32x2, v);
 }
-__device__ __forceinline__ void lds_write8(unsigned char* base, int off, const u32x2& v) {
-  *reinterpret_cast<u32x2*>(base + off) = v;
+
+// Byte address of a shared-memory object as seen by LDS instructions / M0.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  return (uint32_t)(uintptr_t)(lds_u8*)(unsigned char*)p;
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (gfx950 buffer_load_dwordx4
+// ... lds): lane i's bytes land at LDS address m0 + 16 i.  Out-of-range
+// offsets (kOOB) write zeros.  Issued as inline asm so the compiler does not
+// model these LDS writes: completion is tracked explicitly with vmcnt waits
+// before the barrier that publishes a stage.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_base_uniform, int voff) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base_uniform), "v"(voff), "s"(r)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// and all its LDS operations are done, then join the workgroup barrier.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
 // ---------------------------------------------------------------------------

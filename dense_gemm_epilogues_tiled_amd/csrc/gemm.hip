@@ -5,36 +5,38 @@
 // The method is the tiled tensor-core product of the TileLang tutorial
 // ("TileLang: Criando Kernels de GPU de Alto Desempenho ...", noticiai.com.br,
 // section "GEMM com Tensor Cores": operand tiles move global -> shared ->
-// registers, the product runs on the matrix units; section "GEMM com epilogo
-// fundido": bias / ReLU / GELU applied to the accumulator in the same kernel).
-// The tile sizes, pipeline and L2 rasterisation are knobs the spaxe.top page
+// registers, the product runs on the matrix units, the global -> shared copy
+// is pipelined; section "GEMM com epilogo fundido": bias / ReLU / GELU applied
+// to the accumulator in the same kernel, no second pass over C).  Tile sizes,
+// pipeline depth and L2 rasterisation are the knobs the spaxe.top page
 // ("Designing High-Performance GPU Kernels with TileLang ...", schedule
-// paragraph) and the edgex.exchange page (GEMM paragraph: tile sizes,
-// pipeline stages, thread counts, L2 swizzling) name.  The realisation here is
-// gfx950's own:
+// paragraph) and the edgex.exchange page (tiled-GEMM paragraph) name.  The
+// realisation is gfx950's own:
 //   * one workgroup per BM x BN output tile, WAVES_M x WAVES_N wave64s, each
 //     wave owning a (BM/WAVES_M) x (BN/WAVES_N) block of 16x16 MFMA tiles;
-//   * v_mfma_f32_16x16x32_{f16,bf16} with fp32 accumulators in registers;
-//   * 128-bit buffer loads (zero-filled outside the matrix) staged through
-//     registers into a double-buffered, XOR-swizzled LDS ring: the next K step
-//     is fetched from HBM/L2 while the current one feeds the MFMAs;
-//   * row-major B (N contiguous) is transposed in registers on its way into
-//     LDS so both operands are read as k-contiguous 128-bit fragments;
-//   * workgroup ids are regrouped so every XCD (own L2) works on a contiguous
-//     block of tiles, rasterised in bands of GROUP_M tile rows;
-//   * the epilogue runs on the accumulator registers, rounds once and writes
-//     C exactly once.
+//   * v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulators in registers;
+//   * operands go HBM/L2 -> LDS directly (buffer_load_dwordx4 ... lds, no
+//     VGPR staging), STAGES K steps in flight in an LDS ring, one workgroup
+//     barrier per K step; out-of-range rows / columns / k are zero-filled by
+//     the buffer range check (no branches in the loop);
+//   * A (and a k-contiguous B) are read as 128-bit fragments from an
+//     XOR-swizzled layout; a row-major (n-contiguous) B is kept in that
+//     orientation and read with gfx950's transposing ds_read_b64_tr_b16;
+//   * workgroup ids are regrouped so every XCD (private L2) works on a
+//     contiguous band of tiles;
+//   * the epilogue runs on the accumulator registers, rounds once to the
+//     output type and writes C once.
 
 #include "device.hpp"
 #include "kernels.hpp"
 
 namespace tg {
 
-// Workgroup id -> output tile.  Hardware hands consecutive workgroup ids to
-// the 8 XCDs in turn; regroup so XCD x owns logical tiles
+// Workgroup id -> output tile.  The hardware deals consecutive workgroup ids
+// to the 8 XCDs in turn; regroup so XCD x owns logical tiles
 // [x*q + min(x, r), ...) (q = G / 8, r = G % 8), then walk the logical order
-// in bands of group_m tile rows, column by column inside a band, so the tiles
-// an XCD runs at the same time share A rows and B columns in its L2.
+// in bands of group_m tile rows, column by column inside a band, so tiles that
+// run at the same time on one XCD share A rows and B columns in its L2.
 __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int group_m, int xcd_remap, int& tm,
                                          int& tn) {
   const int G = tiles_m * tiles_n;
@@ -52,29 +54,39 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int 
   tn = in / gm;
 }
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool B_COL, class DT>
-__global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(GemmParams p) {
-  static_assert(BK == 64, "LDS layout is written for 64-element K rows");
-  constexpr int NT = WAVES_M * WAVES_N * 64;
-  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
-  constexpr int FM = WTM / 16, FN = WTN / 16;
-  constexpr int KCH = BK / 8;  // 16-byte chunks per K row
-  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
-  constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int A_LOADS = BM * KCH / NT;  // 16-byte A chunks per thread per K step
-  static_assert(A_LOADS * NT == BM * KCH, "A tile must split evenly over the threads");
-  // B, k-contiguous (column-major) source: same scheme as A.
-  constexpr int BC_LOADS = BN * KCH / NT;
-  // B, n-contiguous (row-major) source: units of 4 k-rows x 8 n-columns.
-  constexpr int BR_UNITS = (BK / 4) * (BN / 8) / NT;
-  static_assert(B_COL ? (BC_LOADS * NT == BN * KCH) : (BR_UNITS * NT == (BK / 4) * (BN / 8)),
-                "B tile must split evenly over the threads");
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool B_COL>
+struct GemmShape {
+  static constexpr int NW = WAVES_M * WAVES_N;
+  static constexpr int NT = NW * 64;
+  static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  static constexpr int FM = WTM / 16, FN = WTN / 16;
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int LDS = STAGES * STAGE;
+  // 1 KB direct-to-LDS wave instructions per stage, per wave
+  static constexpr int DA = A_BYTES / 1024 / NW;
+  static constexpr int DB = B_BYTES / 1024 / NW;
+  static constexpr int DMA = DA + DB;
+  static_assert(DA * 1024 * NW == A_BYTES && DB * 1024 * NW == B_BYTES, "tiles must split into 1 KB per wave");
+  static_assert(BK == 32 || BK == 64, "K step of 32 or 64");
+  static_assert(B_COL || BN >= 128, "n-contiguous B tiles need 128+ columns");
+  static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile of whole MFMA tiles");
+  static_assert(LDS <= 160 * 1024, "LDS of one gfx950 CU");
+  static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
+  static_assert((STAGES - 2) * DMA < 64, "vmcnt range");
+};
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool B_COL, class DT>
+__global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(GemmParams p) {
+  using S = GemmShape<BM, BN, BK, WAVES_M, WAVES_N, STAGES, B_COL>;
+  constexpr int NW = S::NW, FM = S::FM, FN = S::FN, DA = S::DA, DB = S::DB;
+  constexpr int KCH = BK / 8;
+
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[S::LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
   int tile_m, tile_n;
@@ -86,107 +98,59 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
   const uint16_t* __restrict__ gA = static_cast<const uint16_t*>(p.A);
   const uint16_t* __restrict__ gB = static_cast<const uint16_t*>(p.B);
 
-  // ---- per-thread load assignments (fixed over the K loop) ----
-  int a_off[A_LOADS], a_lds[A_LOADS];
-  bool a_row_ok[A_LOADS];
-  int a_k8[A_LOADS];
+  // ---- direct-to-LDS copy plan: which global 16 bytes each lane fetches ----
+  // Wave `wave` issues the 1 KB blocks q = wave + NW * j of each region; lane
+  // i of block q fills LDS bytes [1024 q + 16 i, +16) of the region, so the
+  // lane fetches the (row, chunk) the layout stores there.
+  int a_off[DA], a_kc[DA];
+  bool a_ok[DA];
 #pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) {
-    const int q = tid + i * NT, row = q / KCH, c = q % KCH;
-    a_off[i] = row * K * 2 + c * 16;
-    a_lds[i] = lds_off64(row, c);
-    a_row_ok[i] = (m0 + row) < M;
-    a_k8[i] = c * 8;
+  for (int j = 0; j < DA; ++j) {
+    const int pos = 1024 * (wave + NW * j) + 16 * lane;
+    const int row = pos / (BK * 2);
+    const int slot = (pos % (BK * 2)) / 16;
+    const int chunk = slot ^ ((row / (16 / KCH)) % KCH);
+    a_off[j] = row * K * 2 + chunk * 16;
+    a_kc[j] = chunk * 8;
+    a_ok[j] = (m0 + row) < M;
   }
-  constexpr int B_REGS = B_COL ? BC_LOADS : BR_UNITS * 4;
-  int b_off[B_REGS];
-  bool b_ok[B_REGS];
-  int b_k[B_REGS];  // k offset inside the K step of the chunk / row
-  int b_lds[B_COL ? BC_LOADS : 1];
-  if constexpr (B_COL) {
+  int b_off[DB], b_kc[DB];
+  bool b_ok[DB];
 #pragma unroll
-    for (int i = 0; i < BC_LOADS; ++i) {
-      const int q = tid + i * NT, row = q / KCH, c = q % KCH;
-      b_off[i] = row * K * 2 + c * 16;
-      b_lds[i] = lds_off64(row, c);
-      b_ok[i] = (n0 + row) < N;
-      b_k[i] = c * 8;
+  for (int j = 0; j < DB; ++j) {
+    const int pos = 1024 * (wave + NW * j) + 16 * lane;
+    if constexpr (B_COL) {
+      const int row = pos / (BK * 2);  // n
+      const int slot = (pos % (BK * 2)) / 16;
+      const int chunk = slot ^ ((row / (16 / KCH)) % KCH);
+      b_off[j] = row * K * 2 + chunk * 16;
+      b_kc[j] = chunk * 8;
+      b_ok[j] = (n0 + row) < N;
+    } else {
+      const int k = pos / (BN * 2);
+      const int slot = (pos % (BN * 2)) / 16;
+      const int chunk = (((slot >> 1) ^ nc_swz(k)) << 1) | (slot & 1);
+      b_off[j] = k * N * 2 + chunk * 16;
+      b_kc[j] = k;
+      b_ok[j] = (n0 + chunk * 8) < N;
     }
-  } else {
-#pragma unroll
-    for (int u = 0; u < BR_UNITS; ++u) {
-      const int q = tid + u * NT;
-      const int kg = q % (BK / 4), nc = q / (BK / 4);
-      // this thread's rows 4kg..4kg+3, columns 8nc..8nc+7 of the B step
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        b_off[u * 4 + r] = (4 * kg + r) * N * 2 + nc * 16;
-        b_ok[u * 4 + r] = (n0 + 8 * nc) < N;
-        b_k[u * 4 + r] = 4 * kg + r;
-      }
-    }
-    b_lds[0] = 0;
   }
+  const uint32_t smem_base = lds_addr(smem);
 
-  u32x4 ra[A_LOADS];
-  u32x4 rb[B_REGS];
-
-  auto load_step = [&](int kt) {
+  auto issue_stage = [&](int kt, int slot) {
     const int k0 = kt * BK;
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(gA + (size_t)m0 * K + k0);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(B_COL ? gB + (size_t)n0 * K + k0 : gB + (size_t)k0 * N + n0);
+    const uint32_t sbase = smem_base + slot * S::STAGE;
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      const bool ok = a_row_ok[i] && (k0 + a_k8[i]) < K;
-      ra[i] = buffer_load16(rA, ok ? a_off[i] : kOOB);
+    for (int j = 0; j < DA; ++j) {
+      const bool ok = a_ok[j] && (k0 + a_kc[j]) < K;
+      dma16(rA, sbase + 1024 * (wave + NW * j), ok ? a_off[j] : kOOB);
     }
-    if constexpr (B_COL) {
-      const __amdgpu_buffer_rsrc_t rB = make_rsrc(gB + (size_t)n0 * K + k0);
 #pragma unroll
-      for (int i = 0; i < BC_LOADS; ++i) {
-        const bool ok = b_ok[i] && (k0 + b_k[i]) < K;
-        rb[i] = buffer_load16(rB, ok ? b_off[i] : kOOB);
-      }
-    } else {
-      const __amdgpu_buffer_rsrc_t rB = make_rsrc(gB + (size_t)k0 * N + n0);
-#pragma unroll
-      for (int i = 0; i < B_REGS; ++i) {
-        const bool ok = b_ok[i] && (k0 + b_k[i]) < K;
-        rb[i] = buffer_load16(rB, ok ? b_off[i] : kOOB);
-      }
-    }
-  };
-
-  auto store_step = [&](int stage) {
-    unsigned char* sA = smem + stage * STAGE;
-    unsigned char* sB = sA + A_BYTES;
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) lds_write16(sA, a_lds[i], ra[i]);
-    if constexpr (B_COL) {
-#pragma unroll
-      for (int i = 0; i < BC_LOADS; ++i) lds_write16(sB, b_lds[i], rb[i]);
-    } else {
-#pragma unroll
-      for (int u = 0; u < BR_UNITS; ++u) {
-        const int q = tid + u * NT;
-        const int kg = q % (BK / 4), nc = q / (BK / 4);
-        const u32x4& r0 = rb[u * 4 + 0];
-        const u32x4& r1 = rb[u * 4 + 1];
-        const u32x4& r2 = rb[u * 4 + 2];
-        const u32x4& r3 = rb[u * 4 + 3];
-        // column 2d   of the unit: low halves of word d of rows 0..3
-        // column 2d+1 of the unit: high halves of word d of rows 0..3
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          u32x2 ev, od;
-          ev.x = (r0[d] & 0xffffu) | (r1[d] << 16);
-          ev.y = (r2[d] & 0xffffu) | (r3[d] << 16);
-          od.x = (r0[d] >> 16) | (r1[d] & 0xffff0000u);
-          od.y = (r2[d] >> 16) | (r3[d] & 0xffff0000u);
-          const int row_e = 8 * nc + 2 * d;
-          lds_write8(sB, lds_off64(row_e, kg >> 1) + ((kg & 1) << 3), ev);
-          lds_write8(sB, lds_off64(row_e + 1, kg >> 1) + ((kg & 1) << 3), od);
-        }
-      }
+    for (int j = 0; j < DB; ++j) {
+      const bool ok = b_ok[j] && (k0 + b_kc[j]) < K;
+      dma16(rB, sbase + S::A_BYTES + 1024 * (wave + NW * j), ok ? b_off[j] : kOOB);
     }
   };
 
@@ -196,21 +160,32 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // fragment rows of this lane inside the A / B tiles
+  // fragment coordinates of this lane
   const int fr = lane & 15, fk = lane >> 4;
-  const int a_row0 = wm * WTM + fr;
-  const int b_row0 = wn * WTN + fr;
+  const int a_row0 = wm * S::WTM + fr;
 
-  auto compute_step = [&](int stage) {
-    const unsigned char* sA = smem + stage * STAGE;
-    const unsigned char* sB = sA + A_BYTES;
+  auto compute_stage = [&](int slot) {
+    const unsigned char* sA = smem + slot * S::STAGE;
+    const unsigned char* sB = sA + S::A_BYTES;
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
       u32x4 af[FM], bf[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = lds_read16(sA, lds_off64(a_row0 + 16 * i, 4 * kk + fk));
+      for (int i = 0; i < FM; ++i) af[i] = lds_read16(sA, kc_off<BK>(a_row0 + 16 * i, 4 * kk + fk));
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bf[j] = lds_read16(sB, lds_off64(b_row0 + 16 * j, 4 * kk + fk));
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (B_COL) {
+          bf[j] = lds_read16(sB, kc_off<BK>(wn * S::WTN + 16 * j + fr, 4 * kk + fk));
+        } else {
+          // lanes 4q..4q+3 of each 16-lane group read row k = 32kk + 8fk + 4h + q
+          const int nb = wn * S::WTN + 16 * j;  // first column of the MFMA tile
+          const int chunk = nb / 8 + ((fr & 3) >> 1);
+          const int k_lo = 32 * kk + 8 * fk + (fr >> 2);
+          const u32x2 lo = lds_read_tr8(sB, nc_off<BN>(k_lo, chunk) + 8 * (fr & 1));
+          const u32x2 hi = lds_read_tr8(sB, nc_off<BN>(k_lo + 4, chunk) + 8 * (fr & 1));
+          bf[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -218,17 +193,27 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
     }
   };
 
-  if (KT > 0) {
-    load_step(0);
-    store_step(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      const bool more = (kt + 1) < KT;
-      if (more) load_step(kt + 1);
-      compute_step(kt & 1);
-      if (more) store_step((kt + 1) & 1);
-      __syncthreads();
+  // ---- main loop: STAGES-deep ring, one barrier per K step ----
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < KT) issue_stage(s, s);
+  for (int kt = 0; kt < KT; ++kt) {
+    // stage kt's copies are complete once no more than (stages issued after
+    // it) x DMA copies of this wave remain in flight
+    const int later = (KT - 1 - kt) < (STAGES - 2) ? (KT - 1 - kt) : (STAGES - 2);
+    if constexpr (STAGES == 4) {
+      if (later >= 2) wait_vm_barrier<2 * S::DMA>();
+      else if (later == 1) wait_vm_barrier<S::DMA>();
+      else wait_vm_barrier<0>();
+    } else if constexpr (STAGES == 3) {
+      if (later >= 1) wait_vm_barrier<S::DMA>();
+      else wait_vm_barrier<0>();
+    } else {
+      wait_vm_barrier<0>();
     }
+    // every wave is past step kt-1, so its slot can be refilled
+    if (kt + STAGES - 1 < KT) issue_stage(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    compute_stage(kt % STAGES);
   }
 
   // ---- epilogue on the accumulators; lane holds C[m][n .. n+3] per (i, j) ----
@@ -239,7 +224,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
     constexpr int EPI = decltype(epi_tag)::value;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int n = n0 + wn * WTN + 16 * j + 4 * fk;
+      const int n = n0 + wn * S::WTN + 16 * j + 4 * fk;
       if (n >= N) continue;
       float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
       if constexpr (EPI != EPI_NONE) {
@@ -251,7 +236,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int m = m0 + wm * WTM + 16 * i + fr;
+        const int m = m0 + wm * S::WTM + 16 * i + fr;
         if (m >= M) continue;
         const f32x4 a = acc[i][j];
         float x0 = __builtin_fmaf(alpha, a[0], b0);
@@ -285,30 +270,38 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
 }
 
 // ---------------------------------------------------------------------------
-// Launchers for the compiled variants.
+// Compiled variants.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool B_COL, class DT>
+template <int BM, int BN, int BK, int WM, int WN, int ST, bool B_COL, class DT>
 static hipError_t launch_gemm(const GemmParams& p, hipStream_t stream) {
   void* args[] = {const_cast<GemmParams*>(&p)};
-  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(WAVES_M * WAVES_N * 64);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, BK, WAVES_M, WAVES_N, B_COL, DT>),
-                         grid, block, args, 0, stream);
+  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(WM * WN * 64);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, BK, WM, WN, ST, B_COL, DT>), grid,
+                         block, args, 0, stream);
 }
 
-#define TG_GEMM_LAUNCHERS(BM, BN, BK, WM, WN)                                                  \
-  {{                                                                                            \
-    {&launch_gemm<BM, BN, BK, WM, WN, false, F16>, &launch_gemm<BM, BN, BK, WM, WN, true, F16>}, \
-    {&launch_gemm<BM, BN, BK, WM, WN, false, BF16>, &launch_gemm<BM, BN, BK, WM, WN, true, BF16>}   \
-  }}
+template <int BM, int BN, int BK, int WM, int WN, int ST>
+static GemmVariant make_gemm_variant(int group_m) {
+  GemmVariant v;
+  v.cfg = tg_tile_config{0, TG_KERNEL_GEMM, BM, BN, BK, ST, WM * WN, 16, 16, 32, WM, WN, group_m, 1,
+                         GemmShape<BM, BN, BK, WM, WN, ST, false>::LDS, -1};
+  v.fn[0][0] = &launch_gemm<BM, BN, BK, WM, WN, ST, false, F16>;
+  v.fn[0][1] = &launch_gemm<BM, BN, BK, WM, WN, ST, true, F16>;
+  v.fn[1][0] = &launch_gemm<BM, BN, BK, WM, WN, ST, false, BF16>;
+  v.fn[1][1] = &launch_gemm<BM, BN, BK, WM, WN, ST, true, BF16>;
+  return v;
+}
 
-// Order and shapes must match kVariants in api.cpp.  (A host function holding
-// the table keeps the host-only launcher addresses out of device compilation.)
-__host__ const GemmLauncherSet* gemm_launchers(int* count) {
-  static const GemmLauncherSet table[] = {
-      TG_GEMM_LAUNCHERS(128, 128, 64, 2, 2),
-      TG_GEMM_LAUNCHERS(256, 128, 64, 2, 2),
-      TG_GEMM_LAUNCHERS(256, 256, 64, 2, 4),
-      TG_GEMM_LAUNCHERS(128, 64, 64, 2, 1),
+// The compiled GEMM tile configurations, in configuration-id order.  (A host
+// function holding the table keeps host-only launcher addresses out of device
+// compilation.)
+__host__ const GemmVariant* gemm_variants(int* count) {
+  static const GemmVariant table[] = {
+      make_gemm_variant<128, 128, 64, 2, 2, 4>(4),  // 0
+      make_gemm_variant<256, 128, 64, 2, 2, 3>(4),  // 1
+      make_gemm_variant<256, 256, 32, 2, 4, 4>(8),  // 2
+      make_gemm_variant<128, 128, 32, 2, 2, 4>(4),  // 3
+      make_gemm_variant<256, 256, 64, 2, 4, 2>(8),  // 4
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -37,17 +37,20 @@ struct SoftmaxParams {
 typedef hipError_t (*GemmLaunchFn)(const GemmParams&, hipStream_t);
 typedef hipError_t (*SoftmaxLaunchFn)(const SoftmaxParams&, hipStream_t);
 
-// Launchers of one GEMM tile shape: [dtype][b_col_major].
-struct GemmLauncherSet {
+// One compiled GEMM tile configuration: its description and its launchers,
+// indexed [dtype][b_col_major].
+struct GemmVariant {
+  tg_tile_config cfg;
   GemmLaunchFn fn[2][2];
 };
-// Launchers of one softmax shape: [dtype][b_col_major].
-struct SoftmaxLauncherSet {
+// One compiled row-softmax configuration.
+struct SoftmaxVariant {
+  tg_tile_config cfg;
   SoftmaxLaunchFn fn[2][2];
 };
 
-// Launcher tables of the compiled variants (defined next to the kernels).
-const GemmLauncherSet* gemm_launchers(int* count);
-const SoftmaxLauncherSet* softmax_launchers(int* count);
+// Variant tables (defined next to the kernels).
+const GemmVariant* gemm_variants(int* count);
+const SoftmaxVariant* softmax_variants(int* count);
 
 }  // namespace tg

@@ -175,18 +175,25 @@ static hipError_t launch_softmax(const SoftmaxParams& p, hipStream_t stream) {
                          args, 0, stream);
 }
 
-#define TG_SOFTMAX_LAUNCHERS(W, S)                                                           \
-  {{                                                                                          \
-    {&launch_softmax<W, S, false, F16>, &launch_softmax<W, S, true, F16>},                   \
-    {&launch_softmax<W, S, false, BF16>, &launch_softmax<W, S, true, BF16>}                  \
-  }}
+template <int W, int S>
+static SoftmaxVariant make_softmax_variant() {
+  SoftmaxVariant v;
+  // bm = 16 rows per workgroup, bn = longest row, bk = one 32-deep MFMA step
+  v.cfg = tg_tile_config{0, TG_KERNEL_GEMM_SOFTMAX, 16, W * S * 16, 32, 2, W, 16, 16, 32, 1, W, 1, 0,
+                         2 * W * 16 * 4, -1};
+  v.fn[0][0] = &launch_softmax<W, S, false, F16>;
+  v.fn[0][1] = &launch_softmax<W, S, true, F16>;
+  v.fn[1][0] = &launch_softmax<W, S, false, BF16>;
+  v.fn[1][1] = &launch_softmax<W, S, true, BF16>;
+  return v;
+}
 
-// Order and shapes must match the softmax entries of kVariants in api.cpp.
-__host__ const SoftmaxLauncherSet* softmax_launchers(int* count) {
-  static const SoftmaxLauncherSet table[] = {
-      TG_SOFTMAX_LAUNCHERS(4, 16),  // rows up to 1024
-      TG_SOFTMAX_LAUNCHERS(8, 16),  // rows up to 2048
-      TG_SOFTMAX_LAUNCHERS(8, 8),   // rows up to 1024, two waves per SIMD
+// The compiled row-softmax configurations (ids follow the GEMM ones).
+__host__ const SoftmaxVariant* softmax_variants(int* count) {
+  static const SoftmaxVariant table[] = {
+      make_softmax_variant<4, 16>(),  // rows up to 1024
+      make_softmax_variant<8, 16>(),  // rows up to 2048
+      make_softmax_variant<8, 8>(),   // rows up to 1024, two waves per SIMD
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

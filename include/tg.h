@@ -118,9 +118,13 @@ typedef struct tg_tile_config {
   int32_t b_col_major;
 } tg_tile_config;
 
-/* Full argument block of tg_gemm_ex.  config_id < 0 selects from the built-in
- * table; config_id >= 0 forces that compiled configuration (it must be of the
- * right kind and B layout, else TG_ERR_INVALID_ARG). */
+/* Full argument block of tg_gemm_ex.
+ * config_id < 0 selects from the built-in table; config_id >= 0 forces that
+ * compiled configuration (it must be of the right kind, else
+ * TG_ERR_INVALID_ARG).  group_m > 0 overrides the raster band height (tile
+ * rows), 0 keeps the chosen one; xcd_remap 0 / 1 turns the per-XCD tile
+ * regrouping off / on, -1 keeps the chosen setting.  Both only affect which
+ * workgroup computes which tile, never the result. */
 typedef struct tg_gemm_args {
   const void* A;
   const void* B;
@@ -132,6 +136,8 @@ typedef struct tg_gemm_args {
   int32_t b_col_major;
   float alpha;
   int32_t config_id;
+  int32_t group_m;
+  int32_t xcd_remap;
 } tg_gemm_args;
 
 /*

@@ -33,11 +33,32 @@ def stats(g: np.ndarray, y: np.ndarray, out_dtype: str) -> dict:
     }
 
 
-def assert_accept(g: np.ndarray, y: np.ndarray, out_dtype: str, what: str = "") -> dict:
+def rounding_floor(y: np.ndarray, out_dtype: str) -> float:
+    """Relative Frobenius error of the correctly rounded result itself."""
+    if out_dtype == "f32":
+        r = y.astype(np.float32).astype(np.float64)
+    elif out_dtype == "f16":
+        r = y.astype(np.float16).astype(np.float64)
+    else:
+        r = (rne_bf16_bits(y).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ny = np.linalg.norm(y.ravel())
+    return float(np.linalg.norm((r - y).ravel()) / ny) if ny > 0 else 0.0
+
+
+def assert_accept(g: np.ndarray, y: np.ndarray, out_dtype: str, what: str = "", small: bool = False) -> dict:
+    """The acceptance bound.  small=True (edge-case shapes with a few dozen
+    outputs) allows the Frobenius error up to 1.5x that of the correctly
+    rounded answer when that floor alone exceeds the bound: a bf16 result
+    rounded to nearest carries ~1.1e-3 relative RMS error, so on a handful of
+    values the 2e-3 bound is a coin toss even for an exact kernel."""
     s = stats(g, y, out_dtype)
     assert s["finite"], f"{what}: NaN/Inf in GPU output"
     assert s["n_fail"] == 0, f"{what}: {s['n_fail']} of {s['n']} elements outside tolerance, {s}"
-    assert s["frob_rel"] <= FROB, f"{what}: relative Frobenius error {s['frob_rel']:.3e} > {FROB}"
+    bound = FROB
+    if small:
+        bound = max(FROB, 1.5 * rounding_floor(y, out_dtype))
+    s["frob_bound"] = bound
+    assert s["frob_rel"] <= bound, f"{what}: relative Frobenius error {s['frob_rel']:.3e} > {bound:.3e}"
     return s
 
 
@@ -52,6 +73,8 @@ def rne_bf16_bits(y: np.ndarray) -> np.ndarray:
     """Round fp64 -> bfloat16 (8-bit significand), nearest even, for normal-range values."""
     y = np.asarray(y, dtype=np.float64)
     out = np.zeros(y.shape, dtype=np.float64)
+    if not np.any(y != 0):
+        return np.zeros(y.shape, dtype=np.uint16)
     nz = y != 0
     e = np.floor(np.log2(np.abs(y[nz])))
     # guard log2 rounding at exact powers of two

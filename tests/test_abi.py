@@ -17,6 +17,7 @@ import dense_gemm_epilogues_tiled_amd as tg
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tg.h")
+_FIRST_SOFTMAX = min(c["id"] for c in tg.configs() if c["kind"] == tg.TG_KERNEL_GEMM_SOFTMAX)
 
 
 def _declared_functions():
@@ -125,20 +126,22 @@ def test_query_picks_kind_and_layout():
     (dict(C=4098), tg.TG_ERR_MISALIGNED),
     (dict(bias=4104, epilogue=tg.TG_EPI_BIAS_GELU), tg.TG_ERR_MISALIGNED),
     (dict(config_id=99), tg.TG_ERR_INVALID_ARG),
-    (dict(config_id=4), tg.TG_ERR_INVALID_ARG),                             # softmax config for a GEMM
+    (dict(config_id=_FIRST_SOFTMAX), tg.TG_ERR_INVALID_ARG),               # softmax config for a GEMM
     (dict(config_id=0, epilogue=tg.TG_EPI_SOFTMAX), tg.TG_ERR_INVALID_ARG),  # GEMM config for softmax
-    (dict(config_id=4, epilogue=tg.TG_EPI_SOFTMAX, N=2048), tg.TG_ERR_UNSUPPORTED),  # row too long for it
+    (dict(config_id=_FIRST_SOFTMAX, epilogue=tg.TG_EPI_SOFTMAX, N=2048), tg.TG_ERR_UNSUPPORTED),  # row too long
+    (dict(group_m=-1), tg.TG_ERR_INVALID_ARG),
+    (dict(xcd_remap=2), tg.TG_ERR_INVALID_ARG),
 ])
 def test_invalid_arguments_rejected_before_any_hip_call(args, expect):
     # fake, never-dereferenced device addresses: validation must fail first
     base = dict(A=4096, B=8192, bias=None, C=12288, M=64, N=64, K=64, dtype=0, epilogue=0, b_col_major=0,
-                alpha=1.0, config_id=-1)
+                alpha=1.0, config_id=-1, group_m=0, xcd_remap=-1)
     base.update(args)
     if base["bias"] == 0:
         base["bias"] = None
     a = tg.tg_gemm_args(base["A"] or None, base["B"] or None, base["bias"], base["C"] or None, base["M"], base["N"],
                         base["K"], base["dtype"], base["epilogue"], base["b_col_major"], base["alpha"],
-                        base["config_id"])
+                        base["config_id"], base["group_m"], base["xcd_remap"])
     assert tg.tg_gemm_ex(a, None) == expect
 
 

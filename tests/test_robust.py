@@ -12,6 +12,7 @@ from _compare import assert_accept, to_f64
 tg = pytest.importorskip("dense_gemm_epilogues_tiled_amd")
 
 pytestmark = pytest.mark.gpu
+GEMM_IDS = [c["id"] for c in tg.configs() if c["kind"] == tg.TG_KERNEL_GEMM]
 DEV = "cuda:0"
 GUARD = 4096  # elements of canary on each side of C
 
@@ -23,7 +24,7 @@ def _guarded_out(M, N, dtype):
     return buf, buf[GUARD:GUARD + M * N].view(M, N)
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+@pytest.mark.parametrize("cfg", GEMM_IDS)
 def test_no_writes_outside_c(cfg):
     c = tg.configs()[cfg]
     M, N, K = c["bm"] + 3, c["bn"] + 8, 64
@@ -83,4 +84,4 @@ def test_random_shape_sweep():
                      b_col_major=bcol, alpha=0.5)
         torch.cuda.synchronize()
         y = oracle.gemm(A, B, bias, M, N, K, dtype, epi, b_col_major=bcol, alpha=0.5)
-        assert_accept(to_f64(Cd), y, "f32" if epi == "softmax" else dtype, f"sweep {i}")
+        assert_accept(to_f64(Cd), y, "f32" if epi == "softmax" else dtype, f"sweep {i}", small=True)
