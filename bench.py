@@ -129,6 +129,9 @@ def main() -> int:
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-table", action="store_true", help="skip timing the other workloads")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before timing, copy a MIB-sized buffer 3 times (a plain copy kernel of known size "
+                         "whose FETCH_SIZE / WRITE_SIZE counters calibrate HBM traffic readings)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -152,6 +155,16 @@ def main() -> int:
     stream = torch.cuda.Stream(device=dev)
     props = torch.cuda.get_device_properties(dev)
     log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs")
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 copies of {args.copy_calibration} MiB")
+        del src, dst
 
     w = workloads.WORKLOADS[args.workload]
     A, B, bias, Ad, Bd, bd = prepare(w, dev)

@@ -32,6 +32,15 @@
 
 namespace tg {
 
+// Compile-time loop: f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>).
+template <int N, class F, int I = 0>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, F, I + 1>(static_cast<F&&>(f));
+  }
+}
+
 // Workgroup id -> output tile.  The hardware deals consecutive workgroup ids
 // to the 8 XCDs in turn; regroup so XCD x owns logical tiles
 // [x*q + min(x, r), ...) (q = G / 8, r = G % 8), then walk the logical order
@@ -73,7 +82,7 @@ struct GemmShape {
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile of whole MFMA tiles");
   static_assert(LDS <= 160 * 1024, "LDS of one gfx950 CU");
   static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
-  static_assert((STAGES - 2) * DMA < 64, "vmcnt range");
+  static_assert((STAGES - 1) * DMA < 64, "vmcnt range");
 };
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool B_COL, class DT>
@@ -102,20 +111,17 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
   // Wave `wave` issues the 1 KB blocks q = wave + NW * j of each region; lane
   // i of block q fills LDS bytes [1024 q + 16 i, +16) of the region, so the
   // lane fetches the (row, chunk) the layout stores there.
-  int a_off[DA], a_kc[DA];
-  bool a_ok[DA];
+  int a_off[DA], a_kc[DA];  // offset (kOOB for rows past M), k of the chunk
 #pragma unroll
   for (int j = 0; j < DA; ++j) {
     const int pos = 1024 * (wave + NW * j) + 16 * lane;
     const int row = pos / (BK * 2);
     const int slot = (pos % (BK * 2)) / 16;
     const int chunk = slot ^ ((row / (16 / KCH)) % KCH);
-    a_off[j] = row * K * 2 + chunk * 16;
+    a_off[j] = (m0 + row) < M ? row * K * 2 + chunk * 16 : kOOB;
     a_kc[j] = chunk * 8;
-    a_ok[j] = (m0 + row) < M;
   }
   int b_off[DB], b_kc[DB];
-  bool b_ok[DB];
 #pragma unroll
   for (int j = 0; j < DB; ++j) {
     const int pos = 1024 * (wave + NW * j) + 16 * lane;
@@ -123,35 +129,41 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
       const int row = pos / (BK * 2);  // n
       const int slot = (pos % (BK * 2)) / 16;
       const int chunk = slot ^ ((row / (16 / KCH)) % KCH);
-      b_off[j] = row * K * 2 + chunk * 16;
+      b_off[j] = (n0 + row) < N ? row * K * 2 + chunk * 16 : kOOB;
       b_kc[j] = chunk * 8;
-      b_ok[j] = (n0 + row) < N;
     } else {
       const int k = pos / (BN * 2);
       const int slot = (pos % (BN * 2)) / 16;
       const int chunk = (((slot >> 1) ^ nc_swz(k)) << 1) | (slot & 1);
-      b_off[j] = k * N * 2 + chunk * 16;
+      b_off[j] = (n0 + chunk * 8) < N ? k * N * 2 + chunk * 16 : kOOB;
       b_kc[j] = k;
-      b_ok[j] = (n0 + chunk * 8) < N;
     }
   }
   const uint32_t smem_base = lds_addr(smem);
 
-  auto issue_stage = [&](int kt, int slot) {
+  // Copy K step kt into LDS slot `slot`: copies [from, from + count) of the
+  // step's DA + DB wave-wide 1 KB copies (A chunks first, then B).  Steps at
+  // or past the end of K have every chunk out of range: they only write zeros.
+  auto issue_part = [&](int kt, int slot, auto from_c, auto count_c) {
+    constexpr int FROM = decltype(from_c)::value, COUNT = decltype(count_c)::value;
     const int k0 = kt * BK;
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(gA + (size_t)m0 * K + k0);
-    const __amdgpu_buffer_rsrc_t rB = make_rsrc(B_COL ? gB + (size_t)n0 * K + k0 : gB + (size_t)k0 * N + n0);
+    const int k_left = K - k0;  // chunks at k >= k_left are zero-filled
     const uint32_t sbase = smem_base + slot * S::STAGE;
+    if constexpr (FROM < DA) {
+      const __amdgpu_buffer_rsrc_t rA = make_rsrc(gA + (size_t)m0 * K + k0);
 #pragma unroll
-    for (int j = 0; j < DA; ++j) {
-      const bool ok = a_ok[j] && (k0 + a_kc[j]) < K;
-      dma16(rA, sbase + 1024 * (wave + NW * j), ok ? a_off[j] : kOOB);
+      for (int j = FROM; j < DA && j < FROM + COUNT; ++j)
+        dma16(rA, sbase + 1024 * (wave + NW * j), a_kc[j] < k_left ? a_off[j] : kOOB);
     }
+    if constexpr (FROM + COUNT > DA) {
+      const __amdgpu_buffer_rsrc_t rB = make_rsrc(B_COL ? gB + (size_t)n0 * K + k0 : gB + (size_t)k0 * N + n0);
 #pragma unroll
-    for (int j = 0; j < DB; ++j) {
-      const bool ok = b_ok[j] && (k0 + b_kc[j]) < K;
-      dma16(rB, sbase + S::A_BYTES + 1024 * (wave + NW * j), ok ? b_off[j] : kOOB);
+      for (int j = (FROM > DA ? FROM - DA : 0); j < DB && j + DA < FROM + COUNT; ++j)
+        dma16(rB, sbase + S::A_BYTES + 1024 * (wave + NW * j), b_kc[j] < k_left ? b_off[j] : kOOB);
     }
+  };
+  auto issue_stage = [&](int kt, int slot) {
+    issue_part(kt, slot, std::integral_constant<int, 0>{}, std::integral_constant<int, S::DMA>{});
   };
 
   f32x4 acc[FM][FN];
@@ -164,57 +176,173 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
   const int fr = lane & 15, fk = lane >> 4;
   const int a_row0 = wm * S::WTM + fr;
 
-  auto compute_stage = [&](int slot) {
+  // ---- fragments: one 32-deep slice (kk) of a stage ----
+  struct Frags {
+    u32x4 a[FM];
+    u32x4 b[FN];
+  };
+  auto load_frags = [&](int slot, int kk, Frags& f) {
     const unsigned char* sA = smem + slot * S::STAGE;
     const unsigned char* sB = sA + S::A_BYTES;
 #pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      u32x4 af[FM], bf[FN];
+    for (int i = 0; i < FM; ++i) f.a[i] = lds_read16(sA, kc_off<BK>(a_row0 + 16 * i, 4 * kk + fk));
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = lds_read16(sA, kc_off<BK>(a_row0 + 16 * i, 4 * kk + fk));
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        if constexpr (B_COL) {
-          bf[j] = lds_read16(sB, kc_off<BK>(wn * S::WTN + 16 * j + fr, 4 * kk + fk));
-        } else {
-          // lanes 4q..4q+3 of each 16-lane group read row k = 32kk + 8fk + 4h + q
-          const int nb = wn * S::WTN + 16 * j;  // first column of the MFMA tile
-          const int chunk = nb / 8 + ((fr & 3) >> 1);
-          const int k_lo = 32 * kk + 8 * fk + (fr >> 2);
-          const u32x2 lo = lds_read_tr8(sB, nc_off<BN>(k_lo, chunk) + 8 * (fr & 1));
-          const u32x2 hi = lds_read_tr8(sB, nc_off<BN>(k_lo + 4, chunk) + 8 * (fr & 1));
-          bf[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
-        }
+    for (int j = 0; j < FN; ++j) {
+      if constexpr (B_COL) {
+        f.b[j] = lds_read16(sB, kc_off<BK>(wn * S::WTN + 16 * j + fr, 4 * kk + fk));
+      } else {
+        // lanes 4q..4q+3 of each 16-lane group read row k = 32kk + 8fk + 4h + q
+        const int nb = wn * S::WTN + 16 * j;  // first column of the MFMA tile
+        const int chunk = nb / 8 + ((fr & 3) >> 1);
+        const int k_lo = 32 * kk + 8 * fk + (fr >> 2);
+        const u32x2 lo = lds_read_tr8(sB, nc_off<BN>(k_lo, chunk) + 8 * (fr & 1));
+        const u32x2 hi = lds_read_tr8(sB, nc_off<BN>(k_lo + 4, chunk) + 8 * (fr & 1));
+        f.b[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
       }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(DT{}, bf[j], af[i], acc[i][j]);
     }
   };
-
-  // ---- main loop: STAGES-deep ring, one barrier per K step ----
+  auto mfma_frags = [&](const Frags& f) {
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < KT) issue_stage(s, s);
-  for (int kt = 0; kt < KT; ++kt) {
-    // stage kt's copies are complete once no more than (stages issued after
-    // it) x DMA copies of this wave remain in flight
-    const int later = (KT - 1 - kt) < (STAGES - 2) ? (KT - 1 - kt) : (STAGES - 2);
-    if constexpr (STAGES == 4) {
-      if (later >= 2) wait_vm_barrier<2 * S::DMA>();
-      else if (later == 1) wait_vm_barrier<S::DMA>();
-      else wait_vm_barrier<0>();
-    } else if constexpr (STAGES == 3) {
-      if (later >= 1) wait_vm_barrier<S::DMA>();
-      else wait_vm_barrier<0>();
-    } else {
-      wait_vm_barrier<0>();
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(DT{}, f.b[j], f.a[i], acc[i][j]);
+  };
+  // One interleaved phase: the FM*FN MFMAs on `use`, the LDS reads of slice
+  // `kk` of slot `rslot` into `fill`, and copies [FROM, FROM+COUNT) of step
+  // `dkt` into slot `dslot`, spread evenly over the MFMA stream.
+  auto run_phase = [&](const Frags& use, Frags& fill, int rslot, int kk, int dkt, int dslot, auto from_c,
+                       auto count_c) {
+    constexpr int FROM = decltype(from_c)::value, COUNT = decltype(count_c)::value;
+    constexpr int NMF = FM * FN;
+    constexpr int NRD = FM + FN;  // fragment loads (a B load is 1 or 2 instructions)
+    const unsigned char* sA = smem + rslot * S::STAGE;
+    const unsigned char* sB = sA + S::A_BYTES;
+    const int k0 = dkt * BK;
+    const int k_left = K - k0;
+    const uint32_t dbase = smem_base + dslot * S::STAGE;
+    __amdgpu_buffer_rsrc_t rA, rB;
+    if constexpr (COUNT > 0) {
+      rA = make_rsrc(gA + (size_t)m0 * K + k0);
+      rB = make_rsrc(B_COL ? gB + (size_t)n0 * K + k0 : gB + (size_t)k0 * N + n0);
     }
-    // every wave is past step kt-1, so its slot can be refilled
-    if (kt + STAGES - 1 < KT) issue_stage(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-    compute_stage(kt % STAGES);
+    static_for<NMF>([&](auto t_c) {
+      constexpr int t = decltype(t_c)::value;
+      constexpr int i = t / FN, j = t % FN;
+      acc[i][j] = mfma16x16x32(DT{}, use.b[j], use.a[i], acc[i][j]);
+      // fragment loads r with r * NMF / NRD == t, in the order the next phase
+      // first needs them: a0, b0 .. b(FN-1), a1 .. a(FM-1)
+      static_for<NRD>([&](auto r_c) {
+        constexpr int r = decltype(r_c)::value;
+        constexpr bool is_a = (r == 0) || (r > FN);
+        constexpr int ia = r == 0 ? 0 : r - FN;
+        if constexpr ((r * NMF) / NRD == t) {
+          if constexpr (is_a) {
+            fill.a[ia] = lds_read16(sA, kc_off<BK>(a_row0 + 16 * ia, 4 * kk + fk));
+          } else {
+            constexpr int jj = r - 1;
+            if constexpr (B_COL) {
+              fill.b[jj] = lds_read16(sB, kc_off<BK>(wn * S::WTN + 16 * jj + fr, 4 * kk + fk));
+            } else {
+              const int nb = wn * S::WTN + 16 * jj;
+              const int chunk = nb / 8 + ((fr & 3) >> 1);
+              const int k_lo = 32 * kk + 8 * fk + (fr >> 2);
+              const u32x2 lo = lds_read_tr8(sB, nc_off<BN>(k_lo, chunk) + 8 * (fr & 1));
+              const u32x2 hi = lds_read_tr8(sB, nc_off<BN>(k_lo + 4, chunk) + 8 * (fr & 1));
+              fill.b[jj] = u32x4{lo.x, lo.y, hi.x, hi.y};
+            }
+          }
+        }
+      });
+      // copies c with c * NMF / COUNT == t
+      if constexpr (COUNT > 0) {
+        static_for<COUNT>([&](auto c_c) {
+          constexpr int c = decltype(c_c)::value;
+          if constexpr ((c * NMF) / COUNT == t) {
+            constexpr int q = FROM + c;
+            if constexpr (q < DA)
+              dma16(rA, dbase + 1024 * (wave + NW * q), a_kc[q] < k_left ? a_off[q] : kOOB);
+            else
+              dma16(rB, dbase + S::A_BYTES + 1024 * (wave + NW * (q - DA)),
+                    b_kc[q - DA] < k_left ? b_off[q - DA] : kOOB);
+          }
+        });
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // Publish a stage: wait until at most LATER stages of this wave's copies
+  // (those issued after it) are still in flight, then the workgroup barrier.
+  // Every wave waited for its own LDS reads before the barrier, so passing it
+  // also means no wave reads any earlier stage's slot any more.
+  auto publish_first = [&]() { wait_vm_barrier<(STAGES - 1) * S::DMA>(); };
+  auto publish_next = [&]() { wait_vm_barrier<(STAGES - 2) * S::DMA>(); };
+
+  // ---- main loop ----
+  // STAGES steps are in flight before the loop; at every step boundary the
+  // slot just finished is refilled with the step STAGES ahead, so STAGES-1
+  // steps are always in flight while one is computed.  Fragments of the next
+  // 32-deep slice are read from LDS while the MFMAs of the current slice run
+  // (two register buffers F0 / F1 with fixed roles).
+  constexpr int KK = BK / 32;
+  Frags F0, F1;
+  if constexpr (KK == 2) {
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) issue_stage(s, s);
+    issue_part(STAGES - 1, STAGES - 1, std::integral_constant<int, 0>{}, std::integral_constant<int, S::DMA / 2>{});
+  } else {
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) issue_stage(s, s);
   }
+  if (KT > 0) {
+    if constexpr (KK == 2)
+      wait_vm_barrier<(STAGES - 2) * S::DMA + S::DMA / 2>();
+    else
+      publish_first();
+    load_frags(0, 0, F0);
+    if constexpr (KK == 2) {
+      // Explicitly interleaved K step (two 32-deep slices):
+      //   phase A: MFMAs on slice 0 of step kt, interleaved with the LDS reads
+      //            of slice 1 and the second half of the copies of step
+      //            kt+STAGES-1 (into the slot step kt-1 used);
+      //   publish step kt+1 (vmcnt wait + barrier);
+      //   phase B: MFMAs on slice 1, interleaved with the LDS reads of slice 0
+      //            of step kt+1 and the first half of the copies of step
+      //            kt+STAGES (into step kt's slot, free after the barrier).
+      // Between two MFMAs the wave issues at most one LDS read and one copy,
+      // so neither the LDS queue nor the copy queue stalls the MFMA stream;
+      // scheduling fences keep the compiler from regrouping them.
+      for (int kt = 0; kt < KT - 1; ++kt) {
+        const int slot = kt % STAGES;
+        const int prev = (kt + STAGES - 1) % STAGES;
+        run_phase(F0, F1, slot, 1, kt + STAGES - 1, prev, std::integral_constant<int, S::DMA / 2>{},
+                  std::integral_constant<int, S::DMA - S::DMA / 2>{});
+        publish_next();
+        run_phase(F1, F0, (kt + 1) % STAGES, 0, kt + STAGES, slot, std::integral_constant<int, 0>{},
+                  std::integral_constant<int, S::DMA / 2>{});
+      }
+      run_phase(F0, F1, (KT - 1) % STAGES, 1, 0, 0, std::integral_constant<int, 0>{},
+                std::integral_constant<int, 0>{});
+      mfma_frags(F1);
+    } else {
+      int kt = 0;
+      for (; kt + 1 < KT; kt += 2) {
+        publish_next();
+        issue_stage(kt + STAGES, kt % STAGES);
+        load_frags((kt + 1) % STAGES, 0, F1);
+        mfma_frags(F0);
+        if (kt + 2 < KT) {
+          publish_next();
+          issue_stage(kt + 1 + STAGES, (kt + 1) % STAGES);
+          load_frags((kt + 2) % STAGES, 0, F0);
+        }
+        mfma_frags(F1);
+      }
+      if (kt < KT) mfma_frags(F0);
+    }
+  }
+  // copies issued past the end of K may still be writing LDS
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue on the accumulators; lane holds C[m][n .. n+3] per (i, j) ----
   const uint16_t* __restrict__ gbias = static_cast<const uint16_t*>(p.bias);
@@ -302,6 +430,8 @@ __host__ const GemmVariant* gemm_variants(int* count) {
       make_gemm_variant<256, 256, 32, 2, 4, 4>(8),  // 2
       make_gemm_variant<128, 128, 32, 2, 2, 4>(4),  // 3
       make_gemm_variant<256, 256, 64, 2, 4, 2>(8),  // 4
+      make_gemm_variant<128, 128, 64, 2, 4, 4>(4),  // 5: two waves per SIMD
+      make_gemm_variant<128, 128, 64, 4, 2, 4>(4),  // 6
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -176,7 +176,12 @@ def write_table(best, path=TABLE):
         "static const TableEntry kTable[] = {",
     ]
     seen = set()
-    for name, r in sorted(best.items()):
+    # when two workloads share a table key (same dtype, layout, kind and shape),
+    # the headline one decides: the fused bias+GELU 2048^3 case before plain 2048^3
+    priority = ["C3", "C2", "C4a", "C4b", "C5", "C1"]
+    order = sorted(best, key=lambda n: (priority.index(n) if n in priority else len(priority), n))
+    for name in order:
+        r = best[name]
         w = W.WORKLOADS[name]
         dt = "TG_DTYPE_F16" if w.dtype == "f16" else "TG_DTYPE_BF16"
         kind = 1 if w.epilogue == "softmax" else 0
