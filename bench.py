@@ -7,7 +7,9 @@ matrix cores.  One step = one launch of the fused kernel over one batch of
 resident inputs (the whole hot path: tile mapping, pipelined operand staging,
 MFMA main loop, register epilogue, single write of C).
 
-Timing: W eager warmup launches, then K launches captured in one HIP graph
+Timing: W eager warmup launches (default 2000, ~50 ms: the GPU clocks ramp up
+under load, so a short warmup under-reports the steady state), then K launches
+captured in one HIP graph
 (replayed once untimed to upload it), then the timed region: one replay of
 the K-launch graph between torch.cuda.synchronize() calls.  HIP events
 recorded on the launch stream around the same replay give the kernel's
@@ -125,7 +127,9 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=2000,
+                    help="untimed launches before the timed region (about 50 ms at the headline shape, "
+                         "enough for the GPU clocks to settle)")
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-table", action="store_true", help="skip timing the other workloads")

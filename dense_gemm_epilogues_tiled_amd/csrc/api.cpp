@@ -93,14 +93,22 @@ Choice choose(int64_t M, int64_t N, int64_t K, int dtype, int epilogue, int b_co
   for (int i = 0; i < kNumTable; ++i) {
     const TableEntry& e = kTable[i];
     if (e.dtype == dtype && e.b_col_major == b_col_major && e.epilogue_kind == kind && e.M == M && e.N == N &&
-        e.K == K && e.variant >= 0 && e.variant < R.n && R.cfg[e.variant].kind == kind)
+        e.K == K && e.variant >= 0 && e.variant < R.n && R.cfg[e.variant].kind == kind &&
+        (kind == 0 || R.softmax[e.variant - R.n_gemm].fn[dtype][b_col_major]))
       return {e.variant, e.group_m, e.xcd_remap};
   }
   if (kind == 1) {
-    // the softmax variant with the fewest waves whose row capacity covers N
+    // a softmax variant whose row capacity covers N and that has a kernel for
+    // this B layout; variants built for exactly this layout first, then the
+    // fewest waves
     int best = -1;
-    for (int i = R.n_gemm; i < R.n; ++i)
-      if (R.cfg[i].bn >= N && (best < 0 || R.cfg[i].waves < R.cfg[best].waves)) best = i;
+    for (int i = R.n_gemm; i < R.n; ++i) {
+      if (R.cfg[i].bn < N || !R.softmax[i - R.n_gemm].fn[dtype][b_col_major]) continue;
+      const bool exact = R.cfg[i].b_col_major == b_col_major;
+      if (best < 0) { best = i; continue; }
+      const bool best_exact = R.cfg[best].b_col_major == b_col_major;
+      if ((exact && !best_exact) || (exact == best_exact && R.cfg[i].waves < R.cfg[best].waves)) best = i;
+    }
     return {best, 1, 0};
   }
   // the largest tile that still gives every CU at least one tile; failing
@@ -176,6 +184,8 @@ int tg_gemm_ex(const tg_gemm_args* a, void* stream) {
   Choice c;
   if (a->config_id >= 0) {
     if (a->config_id >= R.n || R.cfg[a->config_id].kind != kind) return TG_ERR_INVALID_ARG;
+    if (kind == TG_KERNEL_GEMM_SOFTMAX && !R.softmax[a->config_id - R.n_gemm].fn[a->dtype][a->b_col_major])
+      return TG_ERR_INVALID_ARG;  // variant built for the other B layout
     c = {a->config_id, R.cfg[a->config_id].group_m, R.cfg[a->config_id].xcd_remap};
     if (kind == TG_KERNEL_GEMM_SOFTMAX && a->N > softmax_capacity(R.cfg[a->config_id])) return TG_ERR_UNSUPPORTED;
   } else {

@@ -15,8 +15,8 @@
 // split the row into contiguous column ranges of n_sub 16-wide MFMA tiles
 // each; a wave keeps all of its n_sub 16x16 fp32 accumulator tiles in
 // registers.  Operand fragments come straight from HBM/L2 into registers with
-// 128-bit buffer loads (no LDS: no two waves share a B column), one K step
-// ahead of the MFMAs.  The row max and row sum are reduced first inside each
+// 128-bit buffer loads (no LDS: no two waves share a B column); all loads of
+// a K chunk are issued together and two chunks are in flight.  The row max and row sum are reduced first inside each
 // lane, then across the 4 lanes sharing a row (lane xor 16, xor 32), then
 // across waves through a few bytes of LDS.  exp uses v_exp_f32 (2^x) on
 // (x - max) * log2(e).  Each lane writes 4 consecutive fp32 per tile.
@@ -26,7 +26,7 @@
 
 namespace tg {
 
-template <int WAVES, int MAX_SUB, bool B_COL, class DT>
+template <int WAVES, int MAX_SUB, int KC, bool B_COL, class DT>
 __global__ __launch_bounds__(WAVES * 64, 1) void gemm_softmax_kernel(SoftmaxParams p) {
   __shared__ float red_max[WAVES][16];
   __shared__ float red_sum[WAVES][16];
@@ -44,22 +44,20 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_softmax_kernel(SoftmaxPara
   const uint16_t* __restrict__ gB = static_cast<const uint16_t*>(p.B);
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(gA + (size_t)m0 * K);
   const bool a_row_ok = (m0 + fr) < M;
+  // B offsets stay 32-bit: the descriptor is rebased at this wave's first
+  // column (column-major B) or at the K step's first row (row-major B).
+  const __amdgpu_buffer_rsrc_t rBc = make_rsrc(gB + (size_t)col0 * K);
 
   f32x4 acc[MAX_SUB];
 #pragma unroll
   for (int s = 0; s < MAX_SUB; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int KB = (K + 31) / 32;  // 32-deep MFMA steps
-
-  // fragment loads of one K step
+  // Operand fragments of one 32-deep MFMA step kb: A rows m0..m0+15, B columns
+  // col0 + 16 s .. +15; zero outside the matrix.
   auto load_a = [&](int kb) -> u32x4 {
     const int k = kb * 32 + fk * 8;
-    const bool ok = a_row_ok && k < K;
-    return buffer_load16(rA, ok ? (fr * K + k) * 2 : kOOB);
+    return buffer_load16(rA, (a_row_ok && k < K) ? (fr * K + k) * 2 : kOOB);
   };
-  // B offsets stay 32-bit: the descriptor is rebased at this wave's first
-  // column (column-major B) or at the K step's first row (row-major B).
-  const __amdgpu_buffer_rsrc_t rBc = make_rsrc(gB + (size_t)col0 * K);
   auto load_b = [&](int kb, int s) -> u32x4 {
     const int nl = s * 16 + fr;  // column inside this wave's range
     const int k = kb * 32 + fk * 8;
@@ -85,28 +83,49 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_softmax_kernel(SoftmaxPara
     }
   };
 
-  if (KB > 0) {
-    u32x4 a_cur = load_a(0);
-    u32x4 b_cur[MAX_SUB];
+  // K in chunks of KC steps; all loads of a chunk are issued together and two
+  // chunks are in flight, so the wave waits on memory latency about once.
+  struct Chunk {
+    u32x4 a[KC];
+    u32x4 b[KC][MAX_SUB];
+  };
+  auto load_chunk = [&](int c, Chunk& ch) {
 #pragma unroll
-    for (int s = 0; s < MAX_SUB; ++s) b_cur[s] = load_b(0, s);
-    for (int kb = 0; kb < KB; ++kb) {
-      const bool more = (kb + 1) < KB;
-      u32x4 a_nxt = a_cur;
-      u32x4 b_nxt[MAX_SUB];
-      if (more) {
-        a_nxt = load_a(kb + 1);
+    for (int q = 0; q < KC; ++q) {
+      ch.a[q] = load_a(c * KC + q);
 #pragma unroll
-        for (int s = 0; s < MAX_SUB; ++s) b_nxt[s] = load_b(kb + 1, s);
-      }
-#pragma unroll
-      for (int s = 0; s < MAX_SUB; ++s) acc[s] = mfma16x16x32(DT{}, b_cur[s], a_cur, acc[s]);
-      if (more) {
-        a_cur = a_nxt;
-#pragma unroll
-        for (int s = 0; s < MAX_SUB; ++s) b_cur[s] = b_nxt[s];
-      }
+      for (int s = 0; s < MAX_SUB; ++s) ch.b[q][s] = load_b(c * KC + q, s);
     }
+  };
+  auto mfma_chunk = [&](const Chunk& ch) {
+#pragma unroll
+    for (int q = 0; q < KC; ++q)
+#pragma unroll
+      for (int s = 0; s < MAX_SUB; ++s) acc[s] = mfma16x16x32(DT{}, ch.b[q][s], ch.a[q], acc[s]);
+  };
+  const int NC = (K + 32 * KC - 1) / (32 * KC);
+  if constexpr (!B_COL) {
+    // Row-major B gathers 16-bit values: one K step at a time keeps the
+    // gathered registers small (this layout is not the fast path).
+    const int KB = (K + 31) / 32;
+    for (int kb = 0; kb < KB; ++kb) {
+      const u32x4 a = load_a(kb);
+#pragma unroll
+      for (int s = 0; s < MAX_SUB; ++s) acc[s] = mfma16x16x32(DT{}, load_b(kb, s), a, acc[s]);
+    }
+  } else if (NC > 0) {
+    Chunk c0, c1;
+    load_chunk(0, c0);
+    if (NC > 1) load_chunk(1, c1);
+    int c = 0;
+    for (; c + 2 < NC; c += 2) {
+      mfma_chunk(c0);
+      load_chunk(c + 2, c0);
+      mfma_chunk(c1);
+      if (c + 3 < NC) load_chunk(c + 3, c1);
+    }
+    if (c < NC) mfma_chunk(c0);
+    if (c + 1 < NC) mfma_chunk(c1);
   }
 
   // ---- row softmax on the accumulators ----
@@ -167,33 +186,199 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_softmax_kernel(SoftmaxPara
   }
 }
 
-template <int WAVES, int MAX_SUB, bool B_COL, class DT>
+// ---------------------------------------------------------------------------
+// Column-major B fast path.  Each wave owns NSUB 16-column MFMA tiles of the
+// row (B rows col0 .. col0 + 16 NSUB - 1 of the N x K storage, contiguous in
+// memory) and streams them, one 32-deep K step at a time, HBM/L2 -> its own
+// LDS region with 1 KB direct copies (two steps in flight), together with its
+// own copy of the 16 x 32 A step.  No LDS is shared between waves during the
+// product, so no workgroup barrier is needed there.  LDS rows are 64 bytes
+// (32 k), 16-byte chunks XOR-swizzled by (row / 4) % 4 so 16 consecutive rows
+// at one chunk hit 16 distinct slots.  The softmax result is staged back
+// through the same region so each store instruction writes two contiguous
+// 512-byte row segments.
+// ---------------------------------------------------------------------------
+template <int WAVES, int NSUB, class DT>
+__global__ __launch_bounds__(WAVES * 64, 1) void gemm_softmax_lds_kernel(SoftmaxParams p) {
+  constexpr int SLOT = (1 + NSUB) * 1024;  // one K step: A (16 rows) + NSUB x 16 B rows, 64 B each
+  constexpr int WREG = 2 * SLOT;           // two steps in flight per wave
+  constexpr int DMA = 1 + NSUB;            // 1 KB copies per wave per step
+  constexpr int OUT_STRIDE = NSUB * 64 + 16;  // staged output row (floats of 16 columns x NSUB), padded
+  static_assert(16 * OUT_STRIDE <= WREG, "output staging fits the wave region");
+  static_assert(WAVES * WREG + 2 * WAVES * 16 * 4 <= 160 * 1024, "LDS of one CU");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[WAVES * WREG];
+  __shared__ float red_max[WAVES][16];
+  __shared__ float red_sum[WAVES][16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int fr = lane & 15, fk = lane >> 4;
+  const int M = p.M, N = p.N, K = p.K;
+  const int n_sub = p.n_sub;
+  const int m0 = blockIdx.x * 16;
+  const int col0 = wave * n_sub * 16;
+
+  const uint16_t* __restrict__ gA = static_cast<const uint16_t*>(p.A);
+  const uint16_t* __restrict__ gB = static_cast<const uint16_t*>(p.B);
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(gA + (size_t)m0 * K);
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(gB + (size_t)col0 * K);
+  unsigned char* wreg = smem + wave * WREG;
+  const uint32_t wbase = lds_addr(wreg);
+
+  // Copy plan of one step: copy j (0 = A, 1 + s = B tile s) lane i fills LDS
+  // row 16 j' + i/4 (j' = 0 for A, s for B), physical slot i % 4, i.e. logical
+  // chunk (i % 4) ^ (i / 16); its global source is that row's 8 k values.
+  const int crow = lane >> 2;
+  const int cchunk = (lane & 3) ^ (lane >> 4);
+  const bool a_ok = (m0 + crow) < M;
+  auto issue_step = [&](int kb, int slot) {
+    const int k = kb * 32 + cchunk * 8;
+    const bool k_ok = k < K;
+    const uint32_t sb = wbase + slot * SLOT;
+    dma16(rA, sb, (a_ok && k_ok) ? (crow * K + k) * 2 : kOOB);
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      const int nl = 16 * s + crow;
+      const bool ok = k_ok && s < n_sub && (col0 + nl) < N;
+      dma16(rB, sb + 1024 * (1 + s), ok ? (nl * K + k) * 2 : kOOB);
+    }
+  };
+
+  f32x4 acc[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int KB = (K + 31) / 32;
+  issue_step(0, 0);
+  issue_step(1, 1);
+  for (int kb = 0; kb < KB; ++kb) {
+    const int slot = kb & 1;
+    // step kb is complete once only step kb+1's copies are in flight
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(DMA) : "memory");
+    const unsigned char* sb = wreg + slot * SLOT;
+    const u32x4 a = lds_read16(sb, kc_off<32>(fr, fk));
+    u32x4 b[NSUB];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) b[s] = lds_read16(sb + 1024 * (1 + s), kc_off<32>(fr, fk));
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) acc[s] = mfma16x16x32(DT{}, b[s], a, acc[s]);
+    // the slot is refilled with step kb+2 once this wave's reads of it are done
+    // (steps past the end of K copy nothing but zeros)
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+    issue_step(kb + 2, slot);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+
+  // ---- row softmax on the accumulators (lane: row m0 + fr, columns col0 + 16 s + 4 fk + i) ----
+  const float alpha = p.alpha;
+  const float NEG_INF = -__builtin_inff();
+  float mx = NEG_INF;
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    const int nb = col0 + s * 16 + 4 * fk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = (s < n_sub) && (nb + i) < N;
+      const float x = ok ? alpha * acc[s][i] : NEG_INF;
+      acc[s][i] = x;
+      mx = __builtin_fmaxf(mx, x);
+    }
+  }
+  mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
+  mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+  if (fk == 0) red_max[wave][fr] = mx;
+  __syncthreads();
+  mx = red_max[0][fr];
+#pragma unroll
+  for (int w = 1; w < WAVES; ++w) mx = __builtin_fmaxf(mx, red_max[w][fr]);
+  const float L2E = 1.4426950408889634f;
+  float sum = 0.f;
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = __builtin_amdgcn_exp2f((acc[s][i] - mx) * L2E);  // exp2(-inf) = 0 for padding
+      acc[s][i] = e;
+      sum += e;
+    }
+  }
+  sum += __shfl_xor(sum, 16);
+  sum += __shfl_xor(sum, 32);
+  if (fk == 0) red_sum[wave][fr] = sum;
+  __syncthreads();
+  sum = red_sum[0][fr];
+#pragma unroll
+  for (int w = 1; w < WAVES; ++w) sum += red_sum[w][fr];
+  const float inv = __builtin_amdgcn_rcpf(sum);
+
+  // ---- stage the wave's 16 x 16NSUB block through its LDS region, write rows contiguously ----
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s)
+    *reinterpret_cast<f32x4*>(wreg + fr * OUT_STRIDE + (16 * s + 4 * fk) * 4) = acc[s] * inv;
+  // reads below follow this wave's own writes in LDS order
+  const int cols = (N - col0) < 16 * n_sub ? (N - col0) : 16 * n_sub;  // valid columns of this wave
+  constexpr int LPR = NSUB * 4;          // lanes per staged row (4 floats each)
+  constexpr int RPI = 64 / LPR;          // rows per store instruction
+#pragma unroll
+  for (int q = 0; q < 16 / RPI; ++q) {
+    const int r = q * RPI + lane / LPR;
+    const int c4 = lane % LPR;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(wreg + r * OUT_STRIDE + c4 * 16);
+    if (m0 + r < M && 4 * c4 < cols) *reinterpret_cast<f32x4*>(p.C + (size_t)(m0 + r) * N + col0 + 4 * c4) = v;
+  }
+}
+
+template <int WAVES, int NSUB, class DT>
+static hipError_t launch_softmax_lds(const SoftmaxParams& p, hipStream_t stream) {
+  void* args[] = {const_cast<SoftmaxParams*>(&p)};
+  const dim3 grid((unsigned)((p.M + 15) / 16)), block(WAVES * 64);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_softmax_lds_kernel<WAVES, NSUB, DT>), grid, block, args,
+                         0, stream);
+}
+
+template <int WAVES, int MAX_SUB, int KC, bool B_COL, class DT>
 static hipError_t launch_softmax(const SoftmaxParams& p, hipStream_t stream) {
   void* args[] = {const_cast<SoftmaxParams*>(&p)};
   const dim3 grid((unsigned)((p.M + 15) / 16)), block(WAVES * 64);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_softmax_kernel<WAVES, MAX_SUB, B_COL, DT>), grid, block,
-                         args, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_softmax_kernel<WAVES, MAX_SUB, KC, B_COL, DT>), grid,
+                         block, args, 0, stream);
 }
 
-template <int W, int S>
+template <int W, int S, int KC>
 static SoftmaxVariant make_softmax_variant() {
   SoftmaxVariant v;
   // bm = 16 rows per workgroup, bn = longest row, bk = one 32-deep MFMA step
-  v.cfg = tg_tile_config{0, TG_KERNEL_GEMM_SOFTMAX, 16, W * S * 16, 32, 2, W, 16, 16, 32, 1, W, 1, 0,
+  // bm = 16 rows per workgroup, bn = longest row, bk = one K chunk, stages = chunks in flight
+  v.cfg = tg_tile_config{0, TG_KERNEL_GEMM_SOFTMAX, 16, W * S * 16, 32 * KC, 2, W, 16, 16, 32, 1, W, 1, 0,
                          2 * W * 16 * 4, -1};
-  v.fn[0][0] = &launch_softmax<W, S, false, F16>;
-  v.fn[0][1] = &launch_softmax<W, S, true, F16>;
-  v.fn[1][0] = &launch_softmax<W, S, false, BF16>;
-  v.fn[1][1] = &launch_softmax<W, S, true, BF16>;
+  v.fn[0][0] = &launch_softmax<W, S, KC, false, F16>;
+  v.fn[0][1] = &launch_softmax<W, S, KC, true, F16>;
+  v.fn[1][0] = &launch_softmax<W, S, KC, false, BF16>;
+  v.fn[1][1] = &launch_softmax<W, S, KC, true, BF16>;
+  return v;
+}
+
+template <int W, int S>
+static SoftmaxVariant make_softmax_lds_variant() {
+  SoftmaxVariant v;
+  v.cfg = tg_tile_config{0, TG_KERNEL_GEMM_SOFTMAX, 16, W * S * 16, 32, 2, W, 16, 16, 32, 1, W, 1, 0,
+                         W * 2 * (1 + S) * 1024 + 2 * W * 16 * 4, 1};
+  v.fn[0][0] = nullptr;  // column-major B only
+  v.fn[0][1] = &launch_softmax_lds<W, S, F16>;
+  v.fn[1][0] = nullptr;
+  v.fn[1][1] = &launch_softmax_lds<W, S, BF16>;
   return v;
 }
 
 // The compiled row-softmax configurations (ids follow the GEMM ones).
 __host__ const SoftmaxVariant* softmax_variants(int* count) {
   static const SoftmaxVariant table[] = {
-      make_softmax_variant<4, 16>(),  // rows up to 1024
-      make_softmax_variant<8, 16>(),  // rows up to 2048
-      make_softmax_variant<8, 8>(),   // rows up to 1024, two waves per SIMD
+      make_softmax_variant<8, 8, 2>(),   // rows up to 1024, two waves per SIMD
+      make_softmax_variant<8, 16, 1>(),  // rows up to 2048
+      make_softmax_variant<4, 16, 1>(),  // rows up to 1024, one wave per SIMD
+      make_softmax_lds_variant<8, 8>(),  // rows up to 1024, column-major B through LDS
+      make_softmax_lds_variant<4, 16>(), // rows up to 1024, column-major B through LDS
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -120,8 +120,8 @@ typedef struct tg_tile_config {
 
 /* Full argument block of tg_gemm_ex.
  * config_id < 0 selects from the built-in table; config_id >= 0 forces that
- * compiled configuration (it must be of the right kind, else
- * TG_ERR_INVALID_ARG).  group_m > 0 overrides the raster band height (tile
+ * compiled configuration (it must be of the right kind and, when its
+ * b_col_major is 0 or 1, of that B layout, else TG_ERR_INVALID_ARG).  group_m > 0 overrides the raster band height (tile
  * rows), 0 keeps the chosen one; xcd_remap 0 / 1 turns the per-XCD tile
  * regrouping off / on, -1 keeps the chosen setting.  Both only affect which
  * workgroup computes which tile, never the result. */

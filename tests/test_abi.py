@@ -145,6 +145,13 @@ def test_invalid_arguments_rejected_before_any_hip_call(args, expect):
     assert tg.tg_gemm_ex(a, None) == expect
 
 
+def test_layout_specific_variant_rejects_other_layout():
+    only_col = [c["id"] for c in tg.configs() if c["kind"] == tg.TG_KERNEL_GEMM_SOFTMAX and c["b_col_major"] == 1]
+    assert only_col, "a column-major-only softmax variant is compiled"
+    a = tg.tg_gemm_args(4096, 8192, None, 12288, 64, 64, 64, 0, tg.TG_EPI_SOFTMAX, 0, 1.0, only_col[0], 0, -1)
+    assert tg.tg_gemm_ex(a, None) == tg.TG_ERR_INVALID_ARG
+
+
 def test_null_args_struct():
     assert tg.load().tg_gemm_ex(None, None) == tg.TG_ERR_INVALID_ARG
 
