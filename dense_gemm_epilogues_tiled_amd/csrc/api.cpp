@@ -24,11 +24,12 @@ constexpr int kNumCUs = 256;
 
 // All compiled configurations: the GEMM variants (gemm.hip) with ids
 // 0 .. G-1, then the row-softmax variants (softmax.hip) with ids G ...
+constexpr int kMaxConfigs = 64;
 struct Registry {
   const GemmVariant* gemm;
   const SoftmaxVariant* softmax;
   int n_gemm, n_softmax;
-  tg_tile_config cfg[64];
+  tg_tile_config cfg[kMaxConfigs];
   int n;
 };
 
@@ -36,10 +37,12 @@ const Registry& registry() {
   static const Registry r = [] {
     Registry x{};
     x.gemm = gemm_variants(&x.n_gemm);
+    if (x.n_gemm > kMaxConfigs) x.n_gemm = kMaxConfigs;
     x.softmax = softmax_variants(&x.n_softmax);
+    if (x.n_softmax > kMaxConfigs - x.n_gemm) x.n_softmax = kMaxConfigs - x.n_gemm;
     x.n = 0;
-    for (int i = 0; i < x.n_gemm && x.n < 64; ++i) x.cfg[x.n++] = x.gemm[i].cfg;
-    for (int i = 0; i < x.n_softmax && x.n < 64; ++i) x.cfg[x.n++] = x.softmax[i].cfg;
+    for (int i = 0; i < x.n_gemm; ++i) x.cfg[x.n++] = x.gemm[i].cfg;
+    for (int i = 0; i < x.n_softmax; ++i) x.cfg[x.n++] = x.softmax[i].cfg;
     for (int i = 0; i < x.n; ++i) x.cfg[i].id = i;
     return x;
   }();

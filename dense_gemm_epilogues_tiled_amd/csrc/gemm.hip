@@ -27,41 +27,9 @@
 //   * the epilogue runs on the accumulator registers, rounds once to the
 //     output type and writes C once.
 
-#include "device.hpp"
-#include "kernels.hpp"
+#include "gemm_common.hpp"
 
 namespace tg {
-
-// Compile-time loop: f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>).
-template <int N, class F, int I = 0>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<N, F, I + 1>(static_cast<F&&>(f));
-  }
-}
-
-// Workgroup id -> output tile.  The hardware deals consecutive workgroup ids
-// to the 8 XCDs in turn; regroup so XCD x owns logical tiles
-// [x*q + min(x, r), ...) (q = G / 8, r = G % 8), then walk the logical order
-// in bands of group_m tile rows, column by column inside a band, so tiles that
-// run at the same time on one XCD share A rows and B columns in its L2.
-__device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int group_m, int xcd_remap, int& tm,
-                                         int& tn) {
-  const int G = tiles_m * tiles_n;
-  int w = bid;
-  if (xcd_remap) {
-    const int q = G >> 3, r = G & 7, x = bid & 7, j = bid >> 3;
-    w = x * q + (x < r ? x : r) + j;
-  }
-  const int per_group = group_m * tiles_n;
-  const int g = w / per_group;
-  const int first = g * group_m;
-  const int gm = (tiles_m - first) < group_m ? (tiles_m - first) : group_m;
-  const int in = w - g * per_group;
-  tm = first + in % gm;
-  tn = in / gm;
-}
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool B_COL>
 struct GemmShape {
@@ -88,8 +56,7 @@ struct GemmShape {
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool B_COL, class DT>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(GemmParams p) {
   using S = GemmShape<BM, BN, BK, WAVES_M, WAVES_N, STAGES, B_COL>;
-  constexpr int NW = S::NW, FM = S::FM, FN = S::FN, DA = S::DA, DB = S::DB;
-  constexpr int KCH = BK / 8;
+  constexpr int NW = S::NW, FM = S::FM, FN = S::FN;
 
   __shared__ __attribute__((aligned(1024))) unsigned char smem[S::LDS];
 
@@ -107,38 +74,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
   const uint16_t* __restrict__ gA = static_cast<const uint16_t*>(p.A);
   const uint16_t* __restrict__ gB = static_cast<const uint16_t*>(p.B);
 
-  // ---- direct-to-LDS copy plan: which global 16 bytes each lane fetches ----
-  // Wave `wave` issues the 1 KB blocks q = wave + NW * j of each region; lane
-  // i of block q fills LDS bytes [1024 q + 16 i, +16) of the region, so the
-  // lane fetches the (row, chunk) the layout stores there.
-  int a_off[DA], a_kc[DA];  // offset (kOOB for rows past M), k of the chunk
-#pragma unroll
-  for (int j = 0; j < DA; ++j) {
-    const int pos = 1024 * (wave + NW * j) + 16 * lane;
-    const int row = pos / (BK * 2);
-    const int slot = (pos % (BK * 2)) / 16;
-    const int chunk = slot ^ ((row / (16 / KCH)) % KCH);
-    a_off[j] = (m0 + row) < M ? row * K * 2 + chunk * 16 : kOOB;
-    a_kc[j] = chunk * 8;
-  }
-  int b_off[DB], b_kc[DB];
-#pragma unroll
-  for (int j = 0; j < DB; ++j) {
-    const int pos = 1024 * (wave + NW * j) + 16 * lane;
-    if constexpr (B_COL) {
-      const int row = pos / (BK * 2);  // n
-      const int slot = (pos % (BK * 2)) / 16;
-      const int chunk = slot ^ ((row / (16 / KCH)) % KCH);
-      b_off[j] = (n0 + row) < N ? row * K * 2 + chunk * 16 : kOOB;
-      b_kc[j] = chunk * 8;
-    } else {
-      const int k = pos / (BN * 2);
-      const int slot = (pos % (BN * 2)) / 16;
-      const int chunk = (((slot >> 1) ^ nc_swz(k)) << 1) | (slot & 1);
-      b_off[j] = (n0 + chunk * 8) < N ? k * N * 2 + chunk * 16 : kOOB;
-      b_kc[j] = k;
-    }
-  }
+  CopyPlan<BM, BN, BK, NW, B_COL> plan;
+  plan.init(wave, lane, m0, n0, M, N, K);
   const uint32_t smem_base = lds_addr(smem);
 
   // Copy K step kt into LDS slot `slot`: copies [from, from + count) of the
@@ -146,21 +83,10 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
   // or past the end of K have every chunk out of range: they only write zeros.
   auto issue_part = [&](int kt, int slot, auto from_c, auto count_c) {
     constexpr int FROM = decltype(from_c)::value, COUNT = decltype(count_c)::value;
-    const int k0 = kt * BK;
-    const int k_left = K - k0;  // chunks at k >= k_left are zero-filled
     const uint32_t sbase = smem_base + slot * S::STAGE;
-    if constexpr (FROM < DA) {
-      const __amdgpu_buffer_rsrc_t rA = make_rsrc(gA + (size_t)m0 * K + k0);
-#pragma unroll
-      for (int j = FROM; j < DA && j < FROM + COUNT; ++j)
-        dma16(rA, sbase + 1024 * (wave + NW * j), a_kc[j] < k_left ? a_off[j] : kOOB);
-    }
-    if constexpr (FROM + COUNT > DA) {
-      const __amdgpu_buffer_rsrc_t rB = make_rsrc(B_COL ? gB + (size_t)n0 * K + k0 : gB + (size_t)k0 * N + n0);
-#pragma unroll
-      for (int j = (FROM > DA ? FROM - DA : 0); j < DB && j + DA < FROM + COUNT; ++j)
-        dma16(rB, sbase + S::A_BYTES + 1024 * (wave + NW * j), b_kc[j] < k_left ? b_off[j] : kOOB);
-    }
+    static_for<COUNT>([&](auto c_c) {
+      plan.template copy<FROM + decltype(c_c)::value>(wave, gA, gB, m0, n0, N, K, kt * BK, sbase);
+    });
   };
   auto issue_stage = [&](int kt, int slot) {
     issue_part(kt, slot, std::integral_constant<int, 0>{}, std::integral_constant<int, S::DMA>{});
@@ -174,7 +100,6 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
 
   // fragment coordinates of this lane
   const int fr = lane & 15, fk = lane >> 4;
-  const int a_row0 = wm * S::WTM + fr;
 
   // ---- fragments: one 32-deep slice (kk) of a stage ----
   struct Frags {
@@ -185,21 +110,9 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
     const unsigned char* sA = smem + slot * S::STAGE;
     const unsigned char* sB = sA + S::A_BYTES;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) f.a[i] = lds_read16(sA, kc_off<BK>(a_row0 + 16 * i, 4 * kk + fk));
+    for (int i = 0; i < FM; ++i) f.a[i] = read_a_frag<BK>(sA, wm * S::WTM + 16 * i, kk, fr, fk);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      if constexpr (B_COL) {
-        f.b[j] = lds_read16(sB, kc_off<BK>(wn * S::WTN + 16 * j + fr, 4 * kk + fk));
-      } else {
-        // lanes 4q..4q+3 of each 16-lane group read row k = 32kk + 8fk + 4h + q
-        const int nb = wn * S::WTN + 16 * j;  // first column of the MFMA tile
-        const int chunk = nb / 8 + ((fr & 3) >> 1);
-        const int k_lo = 32 * kk + 8 * fk + (fr >> 2);
-        const u32x2 lo = lds_read_tr8(sB, nc_off<BN>(k_lo, chunk) + 8 * (fr & 1));
-        const u32x2 hi = lds_read_tr8(sB, nc_off<BN>(k_lo + 4, chunk) + 8 * (fr & 1));
-        f.b[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
-      }
-    }
+    for (int j = 0; j < FN; ++j) f.b[j] = read_b_frag<BN, BK, B_COL>(sB, wn * S::WTN + 16 * j, kk, fr, fk);
   };
   auto mfma_frags = [&](const Frags& f) {
 #pragma unroll
@@ -217,14 +130,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
     constexpr int NRD = FM + FN;  // fragment loads (a B load is 1 or 2 instructions)
     const unsigned char* sA = smem + rslot * S::STAGE;
     const unsigned char* sB = sA + S::A_BYTES;
-    const int k0 = dkt * BK;
-    const int k_left = K - k0;
     const uint32_t dbase = smem_base + dslot * S::STAGE;
-    __amdgpu_buffer_rsrc_t rA, rB;
-    if constexpr (COUNT > 0) {
-      rA = make_rsrc(gA + (size_t)m0 * K + k0);
-      rB = make_rsrc(B_COL ? gB + (size_t)n0 * K + k0 : gB + (size_t)k0 * N + n0);
-    }
     static_for<NMF>([&](auto t_c) {
       constexpr int t = decltype(t_c)::value;
       constexpr int i = t / FN, j = t % FN;
@@ -236,35 +142,18 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
         constexpr bool is_a = (r == 0) || (r > FN);
         constexpr int ia = r == 0 ? 0 : r - FN;
         if constexpr ((r * NMF) / NRD == t) {
-          if constexpr (is_a) {
-            fill.a[ia] = lds_read16(sA, kc_off<BK>(a_row0 + 16 * ia, 4 * kk + fk));
-          } else {
-            constexpr int jj = r - 1;
-            if constexpr (B_COL) {
-              fill.b[jj] = lds_read16(sB, kc_off<BK>(wn * S::WTN + 16 * jj + fr, 4 * kk + fk));
-            } else {
-              const int nb = wn * S::WTN + 16 * jj;
-              const int chunk = nb / 8 + ((fr & 3) >> 1);
-              const int k_lo = 32 * kk + 8 * fk + (fr >> 2);
-              const u32x2 lo = lds_read_tr8(sB, nc_off<BN>(k_lo, chunk) + 8 * (fr & 1));
-              const u32x2 hi = lds_read_tr8(sB, nc_off<BN>(k_lo + 4, chunk) + 8 * (fr & 1));
-              fill.b[jj] = u32x4{lo.x, lo.y, hi.x, hi.y};
-            }
-          }
+          if constexpr (is_a)
+            fill.a[ia] = read_a_frag<BK>(sA, wm * S::WTM + 16 * ia, kk, fr, fk);
+          else
+            fill.b[r - 1] = read_b_frag<BN, BK, B_COL>(sB, wn * S::WTN + 16 * (r - 1), kk, fr, fk);
         }
       });
       // copies c with c * NMF / COUNT == t
       if constexpr (COUNT > 0) {
         static_for<COUNT>([&](auto c_c) {
           constexpr int c = decltype(c_c)::value;
-          if constexpr ((c * NMF) / COUNT == t) {
-            constexpr int q = FROM + c;
-            if constexpr (q < DA)
-              dma16(rA, dbase + 1024 * (wave + NW * q), a_kc[q] < k_left ? a_off[q] : kOOB);
-            else
-              dma16(rB, dbase + S::A_BYTES + 1024 * (wave + NW * (q - DA)),
-                    b_kc[q - DA] < k_left ? b_off[q - DA] : kOOB);
-          }
+          if constexpr ((c * NMF) / COUNT == t)
+            plan.template copy<FROM + c>(wave, gA, gB, m0, n0, N, K, dkt * BK, dbase);
         });
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -345,56 +234,9 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue on the accumulators; lane holds C[m][n .. n+3] per (i, j) ----
-  const uint16_t* __restrict__ gbias = static_cast<const uint16_t*>(p.bias);
-  uint16_t* __restrict__ gC = static_cast<uint16_t*>(p.C);
-  const float alpha = p.alpha;
-  auto run_epilogue = [&](auto epi_tag) {
-    constexpr int EPI = decltype(epi_tag)::value;
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n0 + wn * S::WTN + 16 * j + 4 * fk;
-      if (n >= N) continue;
-      float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
-      if constexpr (EPI != EPI_NONE) {
-        const u32x2 bb = *reinterpret_cast<const u32x2*>(gbias + n);
-        b0 = lo_to_f32(DT{}, bb.x);
-        b1 = hi_to_f32(DT{}, bb.x);
-        b2 = lo_to_f32(DT{}, bb.y);
-        b3 = hi_to_f32(DT{}, bb.y);
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int m = m0 + wm * S::WTM + 16 * i + fr;
-        if (m >= M) continue;
-        const f32x4 a = acc[i][j];
-        float x0 = __builtin_fmaf(alpha, a[0], b0);
-        float x1 = __builtin_fmaf(alpha, a[1], b1);
-        float x2 = __builtin_fmaf(alpha, a[2], b2);
-        float x3 = __builtin_fmaf(alpha, a[3], b3);
-        if constexpr (EPI == EPI_RELU) {
-          x0 = __builtin_fmaxf(x0, 0.f);
-          x1 = __builtin_fmaxf(x1, 0.f);
-          x2 = __builtin_fmaxf(x2, 0.f);
-          x3 = __builtin_fmaxf(x3, 0.f);
-        } else if constexpr (EPI == EPI_GELU) {
-          x0 = gelu_erf(x0);
-          x1 = gelu_erf(x1);
-          x2 = gelu_erf(x2);
-          x3 = gelu_erf(x3);
-        }
-        u32x2 out;
-        out.x = pack2(DT{}, x0, x1);
-        out.y = pack2(DT{}, x2, x3);
-        *reinterpret_cast<u32x2*>(gC + (size_t)m * N + n) = out;
-      }
-    }
-  };
-  switch (p.epilogue) {
-    case EPI_RELU: run_epilogue(std::integral_constant<int, EPI_RELU>{}); break;
-    case EPI_GELU: run_epilogue(std::integral_constant<int, EPI_GELU>{}); break;
-    case EPI_BIAS: run_epilogue(std::integral_constant<int, EPI_BIAS>{}); break;
-    default: run_epilogue(std::integral_constant<int, EPI_NONE>{}); break;
-  }
+  with_epilogue(p.epilogue, [&](auto epi_c) {
+    store_tiles<decltype(epi_c)::value, DT, FM, FN, 0, FN>(p, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, fr, fk);
+  });
 }
 
 // ---------------------------------------------------------------------------

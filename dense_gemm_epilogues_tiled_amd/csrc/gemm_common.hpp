@@ -1,0 +1,190 @@
+// gemm_common.hpp -- pieces of the tiled GEMM kernel (gemm.hip): compile-time loops, the workgroup -> tile mapping, the
+// direct-to-LDS copy plan of one K step and the register epilogue.
+#pragma once
+
+#include <type_traits>
+
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace tg {
+
+// Compile-time loop: f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>).
+template <int N, class F, int I = 0>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, F, I + 1>(static_cast<F&&>(f));
+  }
+}
+
+// Workgroup id -> output tile.  The hardware deals consecutive workgroup ids
+// to the 8 XCDs in turn; regroup so XCD x owns logical tiles
+// [x*q + min(x, r), ...) (q = G / 8, r = G % 8), then walk the logical order
+// in bands of group_m tile rows, column by column inside a band, so tiles that
+// run at the same time on one XCD share A rows and B columns in its L2.
+__device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int group_m, int xcd_remap, int& tm,
+                                         int& tn) {
+  const int G = tiles_m * tiles_n;
+  int w = bid;
+  if (xcd_remap) {
+    const int q = G >> 3, r = G & 7, x = bid & 7, j = bid >> 3;
+    w = x * q + (x < r ? x : r) + j;
+  }
+  const int per_group = group_m * tiles_n;
+  const int g = w / per_group;
+  const int first = g * group_m;
+  const int gm = (tiles_m - first) < group_m ? (tiles_m - first) : group_m;
+  const int in = w - g * per_group;
+  tm = first + in % gm;
+  tn = in / gm;
+}
+
+// Direct-to-LDS copy plan of one BM x BK (A) and BK x BN (B) K step for a
+// workgroup of NW waves.  The A tile (and a k-contiguous B tile) is stored in
+// the kc_off layout, an n-contiguous B tile in the nc_off layout.  Wave `wave`
+// issues the 1 KB blocks q = wave + NW * j of each region; lane i of block q
+// fills LDS bytes [1024 q + 16 i, +16) of the region, so the lane fetches the
+// (row, chunk) the layout stores there.  Offsets are relative to the tile's
+// first element of the step; rows / columns past the matrix get kOOB.
+template <int BM, int BN, int BK, int NW, bool B_COL>
+struct CopyPlan {
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  static constexpr int DA = A_BYTES / 1024 / NW;
+  static constexpr int DB = B_BYTES / 1024 / NW;
+  static constexpr int DMA = DA + DB;  // 1 KB copies per wave per K step
+  static_assert(DA * 1024 * NW == A_BYTES && DB * 1024 * NW == B_BYTES, "tiles must split into 1 KB per wave");
+  static_assert(B_COL || BN >= 128, "n-contiguous B tiles need 128+ columns");
+
+  int a_off[DA], a_kc[DA];  // byte offset, first k of the chunk
+  int b_off[DB], b_kc[DB];
+
+  __device__ __forceinline__ void init(int wave, int lane, int m0, int n0, int M, int N, int K) {
+    constexpr int KCH = BK / 8;
+#pragma unroll
+    for (int j = 0; j < DA; ++j) {
+      const int pos = 1024 * (wave + NW * j) + 16 * lane;
+      const int row = pos / (BK * 2);
+      const int slot = (pos % (BK * 2)) / 16;
+      const int chunk = slot ^ ((row / (16 / KCH)) % KCH);
+      a_off[j] = (m0 + row) < M ? row * K * 2 + chunk * 16 : kOOB;
+      a_kc[j] = chunk * 8;
+    }
+#pragma unroll
+    for (int j = 0; j < DB; ++j) {
+      const int pos = 1024 * (wave + NW * j) + 16 * lane;
+      if constexpr (B_COL) {
+        const int row = pos / (BK * 2);  // n
+        const int slot = (pos % (BK * 2)) / 16;
+        const int chunk = slot ^ ((row / (16 / KCH)) % KCH);
+        b_off[j] = (n0 + row) < N ? row * K * 2 + chunk * 16 : kOOB;
+        b_kc[j] = chunk * 8;
+      } else {
+        const int k = pos / (BN * 2);
+        const int slot = (pos % (BN * 2)) / 16;
+        const int chunk = (((slot >> 1) ^ nc_swz(k)) << 1) | (slot & 1);
+        b_off[j] = (n0 + chunk * 8) < N ? k * N * 2 + chunk * 16 : kOOB;
+        b_kc[j] = k;
+      }
+    }
+  }
+
+  // Copy number q (A copies first, then B) of K step starting at k0 into the
+  // stage at LDS byte address `stage`.  Chunks at k >= K are zero-filled, so
+  // steps at or past the end of K only write zeros.
+  template <int Q>
+  __device__ __forceinline__ void copy(int wave, const uint16_t* gA, const uint16_t* gB, int m0, int n0, int N, int K,
+                                       int k0, uint32_t stage) const {
+    const int k_left = K - k0;
+    if constexpr (Q < DA) {
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(gA + (size_t)m0 * K + k0);
+      dma16(r, stage + 1024 * (wave + NW * Q), a_kc[Q] < k_left ? a_off[Q] : kOOB);
+    } else {
+      constexpr int J = Q - DA;
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(B_COL ? gB + (size_t)n0 * K + k0 : gB + (size_t)k0 * N + n0);
+      dma16(r, stage + A_BYTES + 1024 * (wave + NW * J), b_kc[J] < k_left ? b_off[J] : kOOB);
+    }
+  }
+};
+
+// Fragment reads of one 32-deep slice kk of a stage (A tile at sA, B tile at
+// sB).  A fragment: rows r0 .. r0+15 of the A tile; B fragment: columns
+// c0 .. c0+15 of the B tile.  Each lane ends with the 8 k values of its MFMA
+// operand (see mfma16x16x32).
+template <int BK>
+__device__ __forceinline__ u32x4 read_a_frag(const unsigned char* sA, int r0, int kk, int fr, int fk) {
+  return lds_read16(sA, kc_off<BK>(r0 + fr, 4 * kk + fk));
+}
+template <int BN, int BK, bool B_COL>
+__device__ __forceinline__ u32x4 read_b_frag(const unsigned char* sB, int c0, int kk, int fr, int fk) {
+  if constexpr (B_COL) {
+    return lds_read16(sB, kc_off<BK>(c0 + fr, 4 * kk + fk));
+  } else {
+    // lanes 4q..4q+3 of each 16-lane group read row k = 32kk + 8fk + 4h + q
+    const int chunk = c0 / 8 + ((fr & 3) >> 1);
+    const int k_lo = 32 * kk + 8 * fk + (fr >> 2);
+    const u32x2 lo = lds_read_tr8(sB, nc_off<BN>(k_lo, chunk) + 8 * (fr & 1));
+    const u32x2 hi = lds_read_tr8(sB, nc_off<BN>(k_lo + 4, chunk) + 8 * (fr & 1));
+    return u32x4{lo.x, lo.y, hi.x, hi.y};
+  }
+}
+
+// bias[n .. n+3] widened to fp32 (zeros without a bias epilogue).
+template <int EPI, class DT>
+__device__ __forceinline__ f32x4 load_bias4(const GemmParams& p, int n) {
+  if constexpr (EPI == EPI_NONE) {
+    return f32x4{0.f, 0.f, 0.f, 0.f};
+  } else {
+    const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n);
+    return f32x4{lo_to_f32(DT{}, bb.x), hi_to_f32(DT{}, bb.x), lo_to_f32(DT{}, bb.y), hi_to_f32(DT{}, bb.y)};
+  }
+}
+
+// Four consecutive outputs of one row: x = alpha * acc + bias, the
+// activation, one rounding to the output type, packed for one 8-byte store.
+template <int EPI, class DT>
+__device__ __forceinline__ u32x2 finish4(float alpha, const f32x4& a, const f32x4& b) {
+  float x[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = __builtin_fmaf(alpha, a[e], b[e]);
+    if constexpr (EPI == EPI_RELU) x[e] = __builtin_fmaxf(x[e], 0.f);
+    if constexpr (EPI == EPI_GELU) x[e] = gelu_erf(x[e]);
+  }
+  return u32x2{pack2(DT{}, x[0], x[1]), pack2(DT{}, x[2], x[3])};
+}
+
+// Register epilogue of 16x16 MFMA tiles (i, j), i < FM, J0 <= j < J1, of one
+// wave: lane (fr, fk) of tile (i, j) holds C[m_base + 16i + fr][n_base + 16j
+// + 4fk + 0..3].
+template <int EPI, class DT, int FM, int FN, int J0, int J1>
+__device__ __forceinline__ void store_tiles(const GemmParams& p, const f32x4 (&acc)[FM][FN], int m_base, int n_base,
+                                            int fr, int fk) {
+  uint16_t* __restrict__ gC = static_cast<uint16_t*>(p.C);
+  const int M = p.M, N = p.N;
+#pragma unroll
+  for (int j = J0; j < J1; ++j) {
+    const int n = n_base + 16 * j + 4 * fk;
+    if (n >= N) continue;
+    const f32x4 b = load_bias4<EPI, DT>(p, n);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = m_base + 16 * i + fr;
+      if (m >= M) continue;
+      *reinterpret_cast<u32x2*>(gC + (size_t)m * N + n) = finish4<EPI, DT>(p.alpha, acc[i][j], b);
+    }
+  }
+}
+
+// Dispatch the runtime epilogue code to a compile-time one.
+template <class F>
+__device__ __forceinline__ void with_epilogue(int epi, F&& f) {
+  switch (epi) {
+    case EPI_RELU: f(std::integral_constant<int, EPI_RELU>{}); break;
+    case EPI_GELU: f(std::integral_constant<int, EPI_GELU>{}); break;
+    case EPI_BIAS: f(std::integral_constant<int, EPI_BIAS>{}); break;
+    default: f(std::integral_constant<int, EPI_NONE>{}); break;
+  }
+}
+
+}  // namespace tg
