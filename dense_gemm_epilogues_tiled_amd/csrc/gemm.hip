@@ -51,6 +51,7 @@ struct GemmShape {
   static_assert(LDS <= 160 * 1024, "LDS of one gfx950 CU");
   static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
   static_assert((STAGES - 1) * DMA < 64, "vmcnt range");
+  static_assert(BM * BN * 2 <= LDS, "the C image fits in the ring");
 };
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool B_COL, class DT>
@@ -230,12 +231,14 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
       if (kt < KT) mfma_frags(F0);
     }
   }
-  // copies issued past the end of K may still be writing LDS
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // copies issued past the end of K may still be writing LDS; once every
+  // wave is past this barrier the ring is free for the C image
+  wait_vm_barrier<0>();
 
-  // ---- epilogue on the accumulators; lane holds C[m][n .. n+3] per (i, j) ----
+  // ---- epilogue on the accumulators, written to C through LDS ----
   with_epilogue(p.epilogue, [&](auto epi_c) {
-    store_tiles<decltype(epi_c)::value, DT, FM, FN, 0, FN>(p, acc, m0 + wm * S::WTM, n0 + wn * S::WTN, fr, fk);
+    store_tile_staged<decltype(epi_c)::value, DT, BM, BN, S::NT, FM, FN>(p, acc, smem, m0, n0, wm * S::WTM,
+                                                                          wn * S::WTN, fr, fk, tid);
   });
 }
 

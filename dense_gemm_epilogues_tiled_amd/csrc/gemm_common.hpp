@@ -154,25 +154,49 @@ __device__ __forceinline__ u32x2 finish4(float alpha, const f32x4& a, const f32x
   return u32x2{pack2(DT{}, x[0], x[1]), pack2(DT{}, x[2], x[3])};
 }
 
-// Register epilogue of 16x16 MFMA tiles (i, j), i < FM, J0 <= j < J1, of one
-// wave: lane (fr, fk) of tile (i, j) holds C[m_base + 16i + fr][n_base + 16j
-// + 4fk + 0..3].
-template <int EPI, class DT, int FM, int FN, int J0, int J1>
-__device__ __forceinline__ void store_tiles(const GemmParams& p, const f32x4 (&acc)[FM][FN], int m_base, int n_base,
-                                            int fr, int fk) {
-  uint16_t* __restrict__ gC = static_cast<uint16_t*>(p.C);
+// Epilogue through LDS.  Every wave finishes its 16x16 MFMA tiles in
+// registers (lane (fr, fk) of tile (i, j) holds C[r0 + 16i + fr][c0 + 16j +
+// 4fk + 0..3] of the tile), packs them to the output type and writes them into
+// a BM x BN row-major image of the tile in LDS; after a workgroup barrier all
+// NT threads copy the image to C as 16-byte pieces, consecutive lanes taking
+// consecutive pieces of a row, so each store instruction writes whole rows of
+// the tile instead of 16 scattered 32-byte pieces.  In the image the 8-byte
+// unit u of row r sits at unit u ^ (2 (r % 16)): the fragment writes (16 rows
+// at one unit) and the row reads (16 bytes per lane) are both free of bank
+// conflicts, and a 16-byte piece (units 2v, 2v+1) stays contiguous.
+// Requires BM * BN * 2 bytes of LDS no longer in use (the caller has waited
+// for its copies and passed a barrier after its last fragment read).
+template <int BN>
+__device__ __forceinline__ int c_image_off(int r, int u) {
+  return r * (BN * 2) + 8 * (u ^ ((r & 15) << 1));
+}
+
+template <int EPI, class DT, int BM, int BN, int NT, int FM, int FN>
+__device__ __forceinline__ void store_tile_staged(const GemmParams& p, const f32x4 (&acc)[FM][FN],
+                                                  unsigned char* smem, int m0, int n0, int r0, int c0, int fr,
+                                                  int fk, int tid) {
+  static_assert(BM * BN / 8 % NT == 0, "whole rounds of 16-byte pieces");
   const int M = p.M, N = p.N;
 #pragma unroll
-  for (int j = J0; j < J1; ++j) {
-    const int n = n_base + 16 * j + 4 * fk;
-    if (n >= N) continue;
-    const f32x4 b = load_bias4<EPI, DT>(p, n);
+  for (int j = 0; j < FN; ++j) {
+    const int c = c0 + 16 * j + 4 * fk;  // column inside the tile
+    const int n = n0 + c;
+    const f32x4 b = n < N ? load_bias4<EPI, DT>(p, n) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int m = m_base + 16 * i + fr;
-      if (m >= M) continue;
-      *reinterpret_cast<u32x2*>(gC + (size_t)m * N + n) = finish4<EPI, DT>(p.alpha, acc[i][j], b);
+      const int r = r0 + 16 * i + fr;
+      *reinterpret_cast<u32x2*>(smem + c_image_off<BN>(r, c / 4)) = finish4<EPI, DT>(p.alpha, acc[i][j], b);
     }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  uint16_t* __restrict__ gC = static_cast<uint16_t*>(p.C);
+  constexpr int PIECES_PER_ROW = BN / 8;
+#pragma unroll
+  for (int q = tid; q < BM * BN / 8; q += NT) {
+    const int r = q / PIECES_PER_ROW, v = q % PIECES_PER_ROW;
+    const int m = m0 + r, n = n0 + 8 * v;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(smem + c_image_off<BN>(r, 2 * v));
+    if (m < M && n < N) *reinterpret_cast<u32x4*>(gC + (size_t)m * N + n) = val;
   }
 }
 
