@@ -176,40 +176,47 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
   // (two register buffers F0 / F1 with fixed roles).
   constexpr int KK = BK / 32;
   Frags F0, F1;
+  // With two stages every copy of step kt+1 is issued in phase B of step
+  // kt-1 (FRONT), so it has a whole step to land before the barrier that
+  // publishes it; with more stages the copies of a step are split between
+  // two phases (the barrier only waits for copies STAGES-2 steps old).
+  constexpr bool FRONT = STAGES == 2;
+  constexpr int COPIES_A = FRONT ? 0 : S::DMA - S::DMA / 2;  // phase A: tail of step kt+STAGES-1
+  constexpr int COPIES_B = FRONT ? S::DMA : S::DMA / 2;      // phase B: head of step kt+STAGES
   if constexpr (KK == 2) {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s) issue_stage(s, s);
-    issue_part(STAGES - 1, STAGES - 1, std::integral_constant<int, 0>{}, std::integral_constant<int, S::DMA / 2>{});
+    issue_part(STAGES - 1, STAGES - 1, std::integral_constant<int, 0>{}, std::integral_constant<int, COPIES_B>{});
   } else {
 #pragma unroll
     for (int s = 0; s < STAGES; ++s) issue_stage(s, s);
   }
   if (KT > 0) {
     if constexpr (KK == 2)
-      wait_vm_barrier<(STAGES - 2) * S::DMA + S::DMA / 2>();
+      wait_vm_barrier<(STAGES - 2) * S::DMA + COPIES_B>();
     else
       publish_first();
     load_frags(0, 0, F0);
     if constexpr (KK == 2) {
       // Explicitly interleaved K step (two 32-deep slices):
       //   phase A: MFMAs on slice 0 of step kt, interleaved with the LDS reads
-      //            of slice 1 and the second half of the copies of step
-      //            kt+STAGES-1 (into the slot step kt-1 used);
+      //            of slice 1 and the tail of the copies of step kt+STAGES-1
+      //            (into the slot step kt-1 used);
       //   publish step kt+1 (vmcnt wait + barrier);
       //   phase B: MFMAs on slice 1, interleaved with the LDS reads of slice 0
-      //            of step kt+1 and the first half of the copies of step
-      //            kt+STAGES (into step kt's slot, free after the barrier).
+      //            of step kt+1 and the head of the copies of step kt+STAGES
+      //            (into step kt's slot, free after the barrier).
       // Between two MFMAs the wave issues at most one LDS read and one copy,
       // so neither the LDS queue nor the copy queue stalls the MFMA stream;
       // scheduling fences keep the compiler from regrouping them.
       for (int kt = 0; kt < KT - 1; ++kt) {
         const int slot = kt % STAGES;
         const int prev = (kt + STAGES - 1) % STAGES;
-        run_phase(F0, F1, slot, 1, kt + STAGES - 1, prev, std::integral_constant<int, S::DMA / 2>{},
-                  std::integral_constant<int, S::DMA - S::DMA / 2>{});
+        run_phase(F0, F1, slot, 1, kt + STAGES - 1, prev, std::integral_constant<int, COPIES_B>{},
+                  std::integral_constant<int, COPIES_A>{});
         publish_next();
         run_phase(F1, F0, (kt + 1) % STAGES, 0, kt + STAGES, slot, std::integral_constant<int, 0>{},
-                  std::integral_constant<int, S::DMA / 2>{});
+                  std::integral_constant<int, COPIES_B>{});
       }
       run_phase(F0, F1, (KT - 1) % STAGES, 1, 0, 0, std::integral_constant<int, 0>{},
                 std::integral_constant<int, 0>{});
