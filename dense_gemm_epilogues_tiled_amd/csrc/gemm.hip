@@ -54,7 +54,7 @@ struct GemmShape {
   static_assert(BM * BN * 2 <= LDS, "the C image fits in the ring");
 };
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool B_COL, class DT>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool FRONT, bool B_COL, class DT>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(GemmParams p) {
   using S = GemmShape<BM, BN, BK, WAVES_M, WAVES_N, STAGES, B_COL>;
   constexpr int NW = S::NW, FM = S::FM, FN = S::FN;
@@ -176,11 +176,11 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
   // (two register buffers F0 / F1 with fixed roles).
   constexpr int KK = BK / 32;
   Frags F0, F1;
-  // With two stages every copy of step kt+1 is issued in phase B of step
-  // kt-1 (FRONT), so it has a whole step to land before the barrier that
-  // publishes it; with more stages the copies of a step are split between
-  // two phases (the barrier only waits for copies STAGES-2 steps old).
-  constexpr bool FRONT = STAGES == 2;
+  // FRONT: every copy of step kt+STAGES is issued in phase B of step kt,
+  // as soon as its slot is free, so it has STAGES-1 whole steps to land (with
+  // two stages this is what keeps the barrier that publishes step kt+1 from
+  // waiting on copies issued just before it).  Otherwise the copies of a
+  // step are split between phase B of one step and phase A of the next.
   constexpr int COPIES_A = FRONT ? 0 : S::DMA - S::DMA / 2;  // phase A: tail of step kt+STAGES-1
   constexpr int COPIES_B = FRONT ? S::DMA : S::DMA / 2;      // phase B: head of step kt+STAGES
   if constexpr (KK == 2) {
@@ -252,23 +252,23 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
 // ---------------------------------------------------------------------------
 // Compiled variants.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WM, int WN, int ST, bool B_COL, class DT>
+template <int BM, int BN, int BK, int WM, int WN, int ST, bool FRONT, bool B_COL, class DT>
 static hipError_t launch_gemm(const GemmParams& p, hipStream_t stream) {
   void* args[] = {const_cast<GemmParams*>(&p)};
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(WM * WN * 64);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, BK, WM, WN, ST, B_COL, DT>), grid,
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, BK, WM, WN, ST, FRONT, B_COL, DT>), grid,
                          block, args, 0, stream);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int ST>
+template <int BM, int BN, int BK, int WM, int WN, int ST, bool FRONT = ST == 2>
 static GemmVariant make_gemm_variant(int group_m) {
   GemmVariant v;
   v.cfg = tg_tile_config{0, TG_KERNEL_GEMM, BM, BN, BK, ST, WM * WN, 16, 16, 32, WM, WN, group_m, 1,
                          GemmShape<BM, BN, BK, WM, WN, ST, false>::LDS, -1};
-  v.fn[0][0] = &launch_gemm<BM, BN, BK, WM, WN, ST, false, F16>;
-  v.fn[0][1] = &launch_gemm<BM, BN, BK, WM, WN, ST, true, F16>;
-  v.fn[1][0] = &launch_gemm<BM, BN, BK, WM, WN, ST, false, BF16>;
-  v.fn[1][1] = &launch_gemm<BM, BN, BK, WM, WN, ST, true, BF16>;
+  v.fn[0][0] = &launch_gemm<BM, BN, BK, WM, WN, ST, FRONT, false, F16>;
+  v.fn[0][1] = &launch_gemm<BM, BN, BK, WM, WN, ST, FRONT, true, F16>;
+  v.fn[1][0] = &launch_gemm<BM, BN, BK, WM, WN, ST, FRONT, false, BF16>;
+  v.fn[1][1] = &launch_gemm<BM, BN, BK, WM, WN, ST, FRONT, true, BF16>;
   return v;
 }
 
@@ -284,6 +284,7 @@ __host__ const GemmVariant* gemm_variants(int* count) {
       make_gemm_variant<256, 256, 64, 2, 4, 2>(8),  // 4
       make_gemm_variant<128, 128, 64, 2, 4, 4>(4),  // 5: two waves per SIMD
       make_gemm_variant<128, 128, 64, 4, 2, 4>(4),  // 6
+      make_gemm_variant<128, 128, 64, 2, 4, 4, true>(4),  // 7: as 5, copies issued a whole step earlier
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

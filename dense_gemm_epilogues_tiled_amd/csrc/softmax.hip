@@ -348,7 +348,6 @@ static hipError_t launch_softmax(const SoftmaxParams& p, hipStream_t stream) {
 template <int W, int S, int KC>
 static SoftmaxVariant make_softmax_variant() {
   SoftmaxVariant v;
-  // bm = 16 rows per workgroup, bn = longest row, bk = one 32-deep MFMA step
   // bm = 16 rows per workgroup, bn = longest row, bk = one K chunk, stages = chunks in flight
   v.cfg = tg_tile_config{0, TG_KERNEL_GEMM_SOFTMAX, 16, W * S * 16, 32 * KC, 2, W, 16, 16, 32, 1, W, 1, 0,
                          2 * W * 16 * 4, -1};
