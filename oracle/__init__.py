@@ -1,4 +1,5 @@
-"""CPU oracle for Y = epilogue(alpha * A.B + bias) -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for Y = epilogue(alpha * A.B + bias) and the tutorial's vector
+addition and row softmax -- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The GPU library never calls it and
@@ -39,7 +40,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-DTYPES = {"f16": 0, "fp16": 0, "float16": 0, "bf16": 1, "bfloat16": 1}
+DTYPES = {"f16": 0, "fp16": 0, "float16": 0, "bf16": 1, "bfloat16": 1, "f32": 2, "fp32": 2, "float32": 2}
 EPILOGUES = {"none": 0, "bias": 1, "relu": 2, "bias_relu": 2, "gelu": 3, "bias_gelu": 3, "softmax": 4}
 
 _lib = None
@@ -80,6 +81,15 @@ def _load():
     lib.oracle_gemm_sampled.restype = ci
     lib.oracle_max_threads.argtypes = [ci]
     lib.oracle_max_threads.restype = ci
+    vp = ctypes.c_void_p
+    lib.oracle_f32_to_f64.argtypes = [ctypes.c_uint32]
+    lib.oracle_f32_to_f64.restype = ctypes.c_double
+    lib.oracle_round.argtypes = [f64p, vp, i64, ci]
+    lib.oracle_round.restype = ci
+    lib.oracle_vector_add.argtypes = [vp, vp, vp, i64, ci]
+    lib.oracle_vector_add.restype = ci
+    lib.oracle_softmax.argtypes = [vp, f64p, i64, i64, ci, ctypes.c_double, ci]
+    lib.oracle_softmax.restype = ci
     _lib = lib
     return lib
 
@@ -173,4 +183,58 @@ def gemm_sampled(A, B, bias, rows, cols, M: int, N: int, K: int, dtype: str, epi
                                      int(bool(b_col_major)), float(alpha), threads or default_threads())
     if rc != 0:
         raise ValueError("oracle_gemm_sampled rejected its arguments")
+    return y
+
+
+# ---- the bandwidth-bound kernels of the tutorial: vector add, row softmax ----
+
+def _storage(x, dtype: str) -> np.ndarray:
+    """Raw element bits of a torch tensor / numpy array: uint16 for fp16 and
+    bf16, uint32 for fp32."""
+    if DTYPES[dtype] == 2:
+        if hasattr(x, "view") and "torch" in type(x).__module__:
+            import torch
+            x = x.detach().cpu().contiguous().view(torch.int32).numpy()
+        a = np.ascontiguousarray(x)
+        if a.dtype == np.float32 or a.dtype == np.int32:
+            a = a.view(np.uint32)
+        if a.dtype != np.uint32:
+            raise TypeError(f"expected 32-bit storage, got {a.dtype}")
+        return a
+    return _bits(x)
+
+
+def f32_to_f64(bits: int) -> float:
+    return _load().oracle_f32_to_f64(bits)
+
+
+def round_to(x, dtype: str) -> np.ndarray:
+    """Bit patterns of the dtype values nearest to fp64 values x (ties to even)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint32 if DTYPES[dtype] == 2 else np.uint16)
+    if _load().oracle_round(_ptr(x, ctypes.c_double), out.ctypes.data, x.size, DTYPES[dtype]) != 0:
+        raise ValueError("oracle_round rejected its arguments")
+    return out
+
+
+def vector_add(A, B, dtype: str) -> np.ndarray:
+    """C = A + B, correctly rounded to dtype, as bit patterns (uint16 / uint32)."""
+    a, b = _storage(A, dtype).ravel(), _storage(B, dtype).ravel()
+    if a.size != b.size:
+        raise ValueError("A and B differ in length")
+    c = np.empty_like(a)
+    if _load().oracle_vector_add(a.ctypes.data, b.ctypes.data, c.ctypes.data, a.size, DTYPES[dtype]) != 0:
+        raise ValueError("oracle_vector_add rejected its arguments")
+    return c
+
+
+def softmax(X, rows: int, cols: int, dtype: str, alpha: float = 1.0, threads: int | None = None) -> np.ndarray:
+    """Y = row softmax of alpha * X (rows x cols), fp64, unrounded."""
+    x = _storage(X, dtype).ravel()
+    if x.size != rows * cols:
+        raise ValueError("X does not have rows * cols elements")
+    y = np.empty((rows, cols), dtype=np.float64)
+    if _load().oracle_softmax(x.ctypes.data, _ptr(y, ctypes.c_double), rows, cols, DTYPES[dtype], float(alpha),
+                              threads or default_threads()) != 0:
+        raise ValueError("oracle_softmax rejected its arguments")
     return y

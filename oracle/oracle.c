@@ -38,6 +38,9 @@
  *   b_col_major: 0 = B is K x N row-major; 1 = B is stored N x K row-major
  *                (i.e. K x N column-major), element (k, n) at n*K + k.
  * bias may be NULL (treated as zero) for every epilogue.
+ *
+ * The vector addition and the standalone row softmax at the end of this file
+ * also take dtype 2 = IEEE binary32.
  */
 #include <math.h>
 #include <stdint.h>
@@ -237,4 +240,137 @@ int oracle_max_threads(int nthreads) {
 #else
   return 1;
 #endif
+}
+
+/* =========================================================================
+ * The tutorial's two bandwidth-bound kernels (TEST INFRASTRUCTURE ONLY):
+ *   - vector addition C[i] = A[i] + B[i] ("Adicao de vetores: o 'Hello
+ *     World' dos kernels", noticiai.com.br; the edgex.exchange page's
+ *     opening paragraph on vector addition);
+ *   - the standalone row-wise softmax Y = softmax(X) per row (noticiai.com.br,
+ *     section "Softmax por linha e FlashAttention": row max, subtract,
+ *     exponentiate, normalise).
+ * Element types: 0 = binary16, 1 = bfloat16, 2 = binary32.
+ * ========================================================================= */
+
+#define OR_DTYPE_F32 2
+
+/* binary32: 1 sign bit, 8 exponent bits (bias 127), 23 fraction bits. */
+double oracle_f32_to_f64(uint32_t w) {
+  int sign = (w >> 31) & 1;
+  int e = (w >> 23) & 0xff;
+  uint32_t f = w & 0x7fffff;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)f, -149); /* subnormal: f * 2^(1-127-23) */
+  } else if (e == 255) {
+    v = f ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(f + 0x800000u), e - 150); /* (1.f) * 2^(e-127) */
+  }
+  return sign ? -v : v;
+}
+
+/* A binary format with P significand bits (hidden bit included), minimum
+ * normal exponent EMIN, maximum exponent EMAX and exponent bias BIAS. */
+typedef struct {
+  int P, EMIN, EMAX, BIAS, FRAC_BITS, EXP_BITS;
+} fmt_t;
+
+static fmt_t fmt_of(int dtype) {
+  fmt_t f16 = {11, -14, 15, 15, 10, 5}, bf16 = {8, -126, 127, 127, 7, 8}, f32 = {24, -126, 127, 127, 23, 8};
+  return dtype == OR_DTYPE_F16 ? f16 : dtype == OR_DTYPE_BF16 ? bf16 : f32;
+}
+
+/* Round a finite or infinite fp64 value to the nearest representable value
+ * of the format, ties to an even last significand bit, and return its bit
+ * pattern.  The representable values around |x| are the integer multiples of
+ * the quantum 2^(max(E, EMIN) - (P-1)), E = exponent of |x|'s leading bit;
+ * |x| / quantum is exact in fp64, rint() rounds it to an integer with ties to
+ * even (C99, default rounding mode), and a result of 2^(EMAX+1) or more is an
+ * overflow to infinity. */
+static uint32_t round_bits(double x, fmt_t F) {
+  const uint32_t sign = signbit(x) ? 1u : 0u;
+  const uint32_t exp_all = (1u << F.EXP_BITS) - 1;
+  const int width = 1 + F.EXP_BITS + F.FRAC_BITS;
+  uint32_t out;
+  double a = fabs(x);
+  if (isnan(x)) {
+    out = (exp_all << F.FRAC_BITS) | (1u << (F.FRAC_BITS - 1));
+  } else if (a == 0.0) {
+    out = 0;
+  } else {
+    int ex;
+    frexp(a, &ex); /* a = m * 2^ex, m in [0.5, 1): leading bit exponent ex - 1 */
+    int E = ex - 1;
+    if (E < F.EMIN) E = F.EMIN;
+    const double quantum = ldexp(1.0, E - (F.P - 1));
+    const double r = rint(a / quantum);
+    const double v = r * quantum;
+    if (isinf(a) || v >= ldexp(1.0, F.EMAX + 1)) {
+      out = exp_all << F.FRAC_BITS;
+    } else if (v == 0.0) {
+      out = 0;
+    } else {
+      frexp(v, &ex);
+      const int Ev = ex - 1;
+      if (Ev < F.EMIN) { /* subnormal: exponent field 0, fraction = v / 2^(EMIN-(P-1)) */
+        out = (uint32_t)(v / ldexp(1.0, F.EMIN - (F.P - 1)));
+      } else {
+        const uint32_t frac = (uint32_t)(v / ldexp(1.0, Ev - (F.P - 1)) - ldexp(1.0, F.P - 1));
+        out = ((uint32_t)(Ev + F.BIAS) << F.FRAC_BITS) | frac;
+      }
+    }
+  }
+  return (sign << (width - 1)) | out;
+}
+
+static double decode_any(const void* p, int64_t i, int dtype) {
+  if (dtype == OR_DTYPE_F32) return oracle_f32_to_f64(((const uint32_t*)p)[i]);
+  return decode(((const uint16_t*)p)[i], dtype);
+}
+
+static void store_any(void* p, int64_t i, int dtype, uint32_t bits) {
+  if (dtype == OR_DTYPE_F32)
+    ((uint32_t*)p)[i] = bits;
+  else
+    ((uint16_t*)p)[i] = (uint16_t)bits;
+}
+
+/* y[i] = the dtype value nearest to x[i] (ties to even), as bit patterns
+ * (uint16 for binary16 / bfloat16, uint32 for binary32). */
+int oracle_round(const double* x, void* y, int64_t n, int dtype) {
+  if (dtype < 0 || dtype > OR_DTYPE_F32 || n < 0) return -1;
+  const fmt_t F = fmt_of(dtype);
+  for (int64_t i = 0; i < n; ++i) store_any(y, i, dtype, round_bits(x[i], F));
+  return 0;
+}
+
+/* C[i] = A[i] + B[i], correctly rounded to the element type.  The two
+ * operands are decoded exactly and added in fp64; rounding that sum to the
+ * element type gives the correctly rounded sum, because a first rounding to a
+ * format with at least 2p + 2 significand bits (53 >= 2 * 24 + 2) cannot change
+ * the final rounding of a sum to p bits (Figueroa, "When is double rounding
+ * innocuous?", SIGNUM Newsletter 30(3), 1995). */
+int oracle_vector_add(const void* A, const void* B, void* C, int64_t n, int dtype) {
+  if (dtype < 0 || dtype > OR_DTYPE_F32 || n < 0) return -1;
+  const fmt_t F = fmt_of(dtype);
+  for (int64_t i = 0; i < n; ++i)
+    store_any(C, i, dtype, round_bits(decode_any(A, i, dtype) + decode_any(B, i, dtype), F));
+  return 0;
+}
+
+/* Y[r][c] = softmax over c of alpha * X[r][c], in fp64 (unrounded): the
+ * inputs are decoded exactly, scaled, and each row goes through the same
+ * max / exp / sum / divide steps as the GEMM epilogue's row softmax. */
+int oracle_softmax(const void* X, double* Y, int64_t rows, int64_t cols, int dtype, double alpha, int nthreads) {
+  if (dtype < 0 || dtype > OR_DTYPE_F32 || rows < 0 || cols < 0) return -1;
+  set_threads(nthreads);
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    double* y = Y + r * cols;
+    for (int64_t c = 0; c < cols; ++c) y[c] = alpha * decode_any(X, r * cols + c, dtype);
+    softmax_row(y, cols);
+  }
+  return 0;
 }
