@@ -32,6 +32,7 @@ TG_ERR_HIP = -4
 
 TG_DTYPE_F16 = 0
 TG_DTYPE_BF16 = 1
+TG_DTYPE_F32 = 2
 
 TG_EPI_NONE = 0
 TG_EPI_BIAS = 1
@@ -43,12 +44,14 @@ TG_KERNEL_GEMM = 0
 TG_KERNEL_GEMM_SOFTMAX = 1
 
 TG_SOFTMAX_MAX_N = 2048
+TG_ROW_SOFTMAX_MAX_ROW_BYTES = 16384
 
 EPILOGUES = {
     "none": TG_EPI_NONE, "bias": TG_EPI_BIAS, "relu": TG_EPI_BIAS_RELU, "bias_relu": TG_EPI_BIAS_RELU,
     "gelu": TG_EPI_BIAS_GELU, "bias_gelu": TG_EPI_BIAS_GELU, "softmax": TG_EPI_SOFTMAX,
 }
 DTYPES = {torch.float16: TG_DTYPE_F16, torch.bfloat16: TG_DTYPE_BF16}
+STREAM_DTYPES = {torch.float16: TG_DTYPE_F16, torch.bfloat16: TG_DTYPE_BF16, torch.float32: TG_DTYPE_F32}
 
 
 class tg_tile_config(ctypes.Structure):
@@ -77,6 +80,10 @@ _SIGNATURES = {
     "tg_gemm_ex": (ctypes.c_int, [ctypes.POINTER(tg_gemm_args), ctypes.c_void_p]),
     "tg_gemm_query_config": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                             ctypes.c_int, ctypes.c_int, ctypes.POINTER(tg_tile_config)]),
+    "tg_vector_add": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                     ctypes.c_void_p]),
+    "tg_row_softmax": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                      ctypes.c_float, ctypes.c_void_p]),
     "tg_num_configs": (ctypes.c_int, []),
     "tg_get_config": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(tg_tile_config)]),
     "tg_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -127,6 +134,15 @@ def tg_gemm_query_config(M: int, N: int, K: int, dtype: int, epilogue: int, b_co
     out = tg_tile_config()
     rc = load().tg_gemm_query_config(M, N, K, dtype, epilogue, b_col_major, ctypes.byref(out))
     return rc, out
+
+
+def tg_vector_add(A: int | None, B: int | None, C: int | None, n: int, dtype: int, stream: int | None) -> int:
+    return load().tg_vector_add(A, B, C, n, dtype, stream)
+
+
+def tg_row_softmax(X: int | None, Y: int | None, rows: int, cols: int, dtype: int, alpha: float,
+                   stream: int | None) -> int:
+    return load().tg_row_softmax(X, Y, rows, cols, dtype, alpha, stream)
 
 
 def tg_num_configs() -> int:
@@ -195,6 +211,47 @@ def gemm(A: torch.Tensor, B: torch.Tensor, bias: torch.Tensor | None = None, epi
     rc = tg_gemm_ex(args, stream if stream is not None else _stream_handle(A.device))
     if rc != TG_OK:
         raise TgError(rc, "tg_gemm_ex")
+    return out
+
+
+def vector_add(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None,
+               stream: int | None = None) -> torch.Tensor:
+    """C = A + B elementwise on the GPU through tg_vector_add (fp16, bf16 or fp32,
+    contiguous, same shape and dtype; ``out`` may be A or B)."""
+    if A.dtype not in STREAM_DTYPES or B.dtype != A.dtype:
+        raise TypeError("A and B must share one dtype: float16, bfloat16 or float32")
+    if not (A.is_cuda and B.is_cuda) or A.device != B.device:
+        raise ValueError("tensors must be on one GPU")
+    if A.shape != B.shape or not A.is_contiguous() or not B.is_contiguous():
+        raise ValueError("A and B must be contiguous and of one shape")
+    if out is None:
+        out = torch.empty_like(A)
+    elif out.shape != A.shape or out.dtype != A.dtype or not out.is_contiguous() or out.device != A.device:
+        raise ValueError("out has the wrong shape, dtype, layout or device")
+    rc = tg_vector_add(A.data_ptr(), B.data_ptr(), out.data_ptr(), A.numel(), STREAM_DTYPES[A.dtype],
+                       stream if stream is not None else _stream_handle(A.device))
+    if rc != TG_OK:
+        raise TgError(rc, "tg_vector_add")
+    return out
+
+
+def row_softmax(X: torch.Tensor, alpha: float = 1.0, out: torch.Tensor | None = None,
+                stream: int | None = None) -> torch.Tensor:
+    """Y = softmax(alpha * X) along the last dimension of a contiguous 2-D X
+    (fp16, bf16 or fp32) through tg_row_softmax; Y is fp32."""
+    if X.dtype not in STREAM_DTYPES:
+        raise TypeError("X must be float16, bfloat16 or float32")
+    if not X.is_cuda or X.dim() != 2 or not X.is_contiguous():
+        raise ValueError("X must be a contiguous 2-D GPU tensor")
+    rows, cols = X.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32, device=X.device)
+    elif out.shape != X.shape or out.dtype != torch.float32 or not out.is_contiguous() or out.device != X.device:
+        raise ValueError("out has the wrong shape, dtype, layout or device")
+    rc = tg_row_softmax(X.data_ptr(), out.data_ptr(), rows, cols, STREAM_DTYPES[X.dtype], float(alpha),
+                        stream if stream is not None else _stream_handle(X.device))
+    if rc != TG_OK:
+        raise TgError(rc, "tg_row_softmax")
     return out
 
 

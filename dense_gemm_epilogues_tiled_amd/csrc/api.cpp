@@ -247,6 +247,37 @@ int tg_gemm_ex(const tg_gemm_args* a, void* stream) {
   return err == hipSuccess ? TG_OK : TG_ERR_HIP;
 }
 
+int tg_vector_add(const void* A, const void* B, void* C, int64_t n, int dtype, void* stream) {
+  if (n < 0) return TG_ERR_INVALID_ARG;
+  const VectorAddFn fn = vector_add_launcher(dtype);
+  if (!fn) return TG_ERR_INVALID_ARG;
+  if (n == 0) return TG_OK;
+  if (!A || !B || !C) return TG_ERR_INVALID_ARG;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return TG_ERR_MISALIGNED;
+  const hipError_t err = fn(VectorAddParams{A, B, C, n}, static_cast<hipStream_t>(stream));
+  if (log_enabled())
+    fprintf(stderr, "tg: vector_add n=%lld dtype=%d -> %s\n", (long long)n, dtype, hipGetErrorString(err));
+  return err == hipSuccess ? TG_OK : TG_ERR_HIP;
+}
+
+int tg_row_softmax(const void* X, float* Y, int64_t rows, int64_t cols, int dtype, float alpha, void* stream) {
+  if (rows < 0 || cols < 0) return TG_ERR_INVALID_ARG;
+  if (dtype != TG_DTYPE_F16 && dtype != TG_DTYPE_BF16 && dtype != TG_DTYPE_F32) return TG_ERR_INVALID_ARG;
+  const int64_t esize = dtype == TG_DTYPE_F32 ? 4 : 2;
+  if (rows >= (int64_t(1) << 31) || cols * esize > TG_ROW_SOFTMAX_MAX_ROW_BYTES) return TG_ERR_UNSUPPORTED;
+  if ((cols * esize) % 16 != 0) return TG_ERR_MISALIGNED;
+  if (rows == 0 || cols == 0) return TG_OK;
+  if (!X || !Y) return TG_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(Y)) return TG_ERR_MISALIGNED;
+  const RowSoftmaxFn fn = row_softmax_launcher(dtype, cols);
+  if (!fn) return TG_ERR_UNSUPPORTED;
+  const hipError_t err = fn(RowSoftmaxParams{X, Y, rows, cols, alpha}, static_cast<hipStream_t>(stream));
+  if (log_enabled())
+    fprintf(stderr, "tg: row_softmax rows=%lld cols=%lld dtype=%d -> %s\n", (long long)rows, (long long)cols, dtype,
+            hipGetErrorString(err));
+  return err == hipSuccess ? TG_OK : TG_ERR_HIP;
+}
+
 int tg_gemm(const void* A, const void* B, const void* bias, void* C, int64_t M, int64_t N, int64_t K, int dtype,
             int epilogue, void* stream) {
   tg_gemm_args a;

@@ -1,5 +1,5 @@
 // kernels.hpp -- interface between the host dispatch (api.cpp) and the
-// compiled kernel variants (gemm.hip, softmax.hip).
+// compiled kernel variants (gemm.hip, softmax.hip, stream.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -33,6 +33,29 @@ struct SoftmaxParams {
   float alpha;
   int n_sub;  // 16-column MFMA tiles per wave: ceil(N / (16 * waves))
 };
+
+// Kernel arguments of the vector addition (stream.hip).
+struct VectorAddParams {
+  const void* A;
+  const void* B;
+  void* C;
+  int64_t n;
+};
+
+// Kernel arguments of the standalone row softmax (stream.hip).
+struct RowSoftmaxParams {
+  const void* X;
+  float* Y;
+  int64_t rows, cols;
+  float alpha;
+};
+
+typedef hipError_t (*VectorAddFn)(const VectorAddParams&, hipStream_t);
+typedef hipError_t (*RowSoftmaxFn)(const RowSoftmaxParams&, hipStream_t);
+
+// Launchers for a dtype (and row length); NULL when unsupported.
+VectorAddFn vector_add_launcher(int dtype);
+RowSoftmaxFn row_softmax_launcher(int dtype, int64_t cols);
 
 typedef hipError_t (*GemmLaunchFn)(const GemmParams&, hipStream_t);
 typedef hipError_t (*SoftmaxLaunchFn)(const SoftmaxParams&, hipStream_t);

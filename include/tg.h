@@ -71,6 +71,10 @@ extern "C" {
 /* Longest softmax row the on-chip row kernel holds (fp32 values per row). */
 #define TG_SOFTMAX_MAX_N 2048
 
+/* Longest row tg_row_softmax holds in registers, in bytes of X: 8192 fp16 /
+ * bf16 elements or 4096 fp32 elements. */
+#define TG_ROW_SOFTMAX_MAX_ROW_BYTES 16384
+
 typedef enum tg_status {
   TG_OK = 0,
   TG_ERR_INVALID_ARG = -1, /* NULL pointer, negative size, unknown enum, bad config id */
@@ -79,7 +83,10 @@ typedef enum tg_status {
   TG_ERR_HIP = -4          /* the HIP runtime rejected the launch */
 } tg_status;
 
-typedef enum tg_dtype { TG_DTYPE_F16 = 0, TG_DTYPE_BF16 = 1 } tg_dtype;
+/* Element types.  The GEMM entry points take TG_DTYPE_F16 and TG_DTYPE_BF16
+ * only (TG_DTYPE_F32 there is TG_ERR_INVALID_ARG); the two bandwidth-bound
+ * kernels at the end of this header also take TG_DTYPE_F32. */
+typedef enum tg_dtype { TG_DTYPE_F16 = 0, TG_DTYPE_BF16 = 1, TG_DTYPE_F32 = 2 } tg_dtype;
 
 typedef enum tg_epilogue {
   TG_EPI_NONE = 0,
@@ -165,6 +172,51 @@ int tg_gemm_ex(const tg_gemm_args* args, void* stream);
  */
 int tg_gemm_query_config(int64_t M, int64_t N, int64_t K, int dtype, int epilogue, int b_col_major,
                          tg_tile_config* out);
+
+/*
+ * tg_vector_add -- C[i] = A[i] + B[i] for 0 <= i < n.
+ *
+ * The tutorial's first kernel ("TileLang: Criando Kernels de GPU de Alto
+ * Desempenho ..." (noticiai.com.br), section "Adicao de vetores: o 'Hello
+ * World' dos kernels"; the edgex.exchange page's opening paragraph on vector
+ * addition).  It is bound by HBM bandwidth and serves as the bandwidth probe
+ * that the fused epilogues are measured against.
+ *
+ *  dtype   TG_DTYPE_F16, TG_DTYPE_BF16 or TG_DTYPE_F32; A, B and C all of it.
+ *          The sum is formed in fp32 and rounded once, to nearest even: for
+ *          every dtype C[i] is the correctly rounded value of A[i] + B[i].
+ *  Layout  three contiguous vectors of n elements, device memory owned by the
+ *          caller, 16-byte aligned.  C may be A or B (in place) but must not
+ *          partly overlap either.
+ *  n       any n >= 0 (no multiple required); n == 0 launches nothing.
+ *  Errors  NULL pointer with n > 0, negative n or unknown dtype:
+ *          TG_ERR_INVALID_ARG; misaligned pointer: TG_ERR_MISALIGNED; a
+ *          rejected launch: TG_ERR_HIP.  One kernel is enqueued on `stream`.
+ */
+int tg_vector_add(const void* A, const void* B, void* C, int64_t n, int dtype, void* stream);
+
+/*
+ * tg_row_softmax -- the standalone row-wise softmax, Y = softmax(alpha X) per row:
+ *
+ *     m_r = max_c alpha X[r][c],   Y[r][c] = exp(alpha X[r][c] - m_r) / sum_c' exp(alpha X[r][c'] - m_r)
+ *
+ * ("TileLang: Criando Kernels ..." (noticiai.com.br), section "Softmax por
+ * linha e FlashAttention": row max, subtract, exponentiate, sum, divide; the
+ * same operation as TG_EPI_SOFTMAX without the product in front of it.)
+ *
+ *  dtype   of X: TG_DTYPE_F16, TG_DTYPE_BF16 or TG_DTYPE_F32.  Y is always
+ *          fp32.  All arithmetic is fp32.
+ *  Layout  X is rows x cols row-major, Y is rows x cols row-major fp32; device
+ *          memory owned by the caller, 16-byte aligned, not overlapping.
+ *  Limits  cols * sizeof(X element) <= TG_ROW_SOFTMAX_MAX_ROW_BYTES, else
+ *          TG_ERR_UNSUPPORTED; rows < 2^31.  A row must be a whole number of
+ *          16-byte pieces (cols a multiple of 8 for fp16 / bf16, of 4 for
+ *          fp32), else TG_ERR_MISALIGNED.  rows == 0 or cols == 0 launches
+ *          nothing.  A row whose entries are all -inf gives NaN, as the
+ *          formula does.
+ *  Errors  as tg_vector_add.  One kernel is enqueued on `stream`.
+ */
+int tg_row_softmax(const void* X, float* Y, int64_t rows, int64_t cols, int dtype, float alpha, void* stream);
 
 /* Number of compiled tile configurations (ids 0 .. n-1). */
 int tg_num_configs(void);

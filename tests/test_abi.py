@@ -29,7 +29,7 @@ def _declared_functions():
 def test_header_declares_expected_entry_points():
     names = _declared_functions()
     for n in ("tg_gemm", "tg_gemm_ex", "tg_gemm_query_config", "tg_num_configs", "tg_get_config",
-              "tg_status_string", "tg_version"):
+              "tg_status_string", "tg_version", "tg_vector_add", "tg_row_softmax"):
         assert n in names
 
 
@@ -105,7 +105,8 @@ def test_query_picks_kind_and_layout():
     (dict(M=-1), tg.TG_ERR_INVALID_ARG),
     (dict(N=-8), tg.TG_ERR_INVALID_ARG),
     (dict(K=-8), tg.TG_ERR_INVALID_ARG),
-    (dict(dtype=2), tg.TG_ERR_INVALID_ARG),
+    (dict(dtype=tg.TG_DTYPE_F32), tg.TG_ERR_INVALID_ARG),  # fp32 is for the bandwidth kernels only
+    (dict(dtype=7), tg.TG_ERR_INVALID_ARG),
     (dict(epilogue=5), tg.TG_ERR_INVALID_ARG),
     (dict(epilogue=-1), tg.TG_ERR_INVALID_ARG),
     (dict(b_col_major=2), tg.TG_ERR_INVALID_ARG),
@@ -179,3 +180,75 @@ def test_torch_wrapper_checks_before_launch():
         tg.gemm(a.float(), a.float())
     with pytest.raises(ValueError):
         tg.gemm(a, a, epilogue="tanh")
+
+
+# ---- the two bandwidth-bound entry points --------------------------------------
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(n=-1), tg.TG_ERR_INVALID_ARG),
+    (dict(dtype=3), tg.TG_ERR_INVALID_ARG),
+    (dict(dtype=-1), tg.TG_ERR_INVALID_ARG),
+    (dict(A=0), tg.TG_ERR_INVALID_ARG),
+    (dict(B=0), tg.TG_ERR_INVALID_ARG),
+    (dict(C=0), tg.TG_ERR_INVALID_ARG),
+    (dict(A=4100), tg.TG_ERR_MISALIGNED),
+    (dict(B=8200), tg.TG_ERR_MISALIGNED),
+    (dict(C=12290), tg.TG_ERR_MISALIGNED),
+])
+def test_vector_add_rejects_before_any_hip_call(args, expect):
+    base = dict(A=4096, B=8192, C=12288, n=1000, dtype=tg.TG_DTYPE_F32)
+    base.update(args)
+    assert tg.tg_vector_add(base["A"] or None, base["B"] or None, base["C"] or None, base["n"], base["dtype"],
+                            None) == expect
+
+
+def test_vector_add_empty_launches_nothing():
+    for dt in (tg.TG_DTYPE_F16, tg.TG_DTYPE_BF16, tg.TG_DTYPE_F32):
+        assert tg.tg_vector_add(None, None, None, 0, dt, None) == tg.TG_OK
+    assert tg.tg_vector_add(None, None, None, 0, 5, None) == tg.TG_ERR_INVALID_ARG  # dtype still checked
+
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(rows=-1), tg.TG_ERR_INVALID_ARG),
+    (dict(cols=-8), tg.TG_ERR_INVALID_ARG),
+    (dict(dtype=3), tg.TG_ERR_INVALID_ARG),
+    (dict(X=0), tg.TG_ERR_INVALID_ARG),
+    (dict(Y=0), tg.TG_ERR_INVALID_ARG),
+    (dict(X=4104), tg.TG_ERR_MISALIGNED),
+    (dict(Y=8196), tg.TG_ERR_MISALIGNED),
+    (dict(cols=12), tg.TG_ERR_MISALIGNED),                                  # fp16 rows of 24 bytes
+    (dict(cols=6, dtype=tg.TG_DTYPE_F32), tg.TG_ERR_MISALIGNED),            # fp32 rows of 24 bytes
+    (dict(cols=8200), tg.TG_ERR_UNSUPPORTED),                               # beyond 16 KiB of fp16
+    (dict(cols=4100, dtype=tg.TG_DTYPE_F32), tg.TG_ERR_UNSUPPORTED),        # beyond 16 KiB of fp32
+    (dict(rows=1 << 31), tg.TG_ERR_UNSUPPORTED),
+])
+def test_row_softmax_rejects_before_any_hip_call(args, expect):
+    base = dict(X=4096, Y=8192, rows=16, cols=64, dtype=tg.TG_DTYPE_F16, alpha=1.0)
+    base.update(args)
+    assert tg.tg_row_softmax(base["X"] or None, base["Y"] or None, base["rows"], base["cols"], base["dtype"],
+                             base["alpha"], None) == expect
+
+
+def test_row_softmax_limits_match_header():
+    assert tg.TG_ROW_SOFTMAX_MAX_ROW_BYTES == 16384
+    src = open(HEADER).read()
+    assert re.search(r"#define TG_ROW_SOFTMAX_MAX_ROW_BYTES 16384\b", src)
+    assert re.search(r"TG_DTYPE_F32 = 2\b", src) and tg.TG_DTYPE_F32 == 2
+
+
+def test_row_softmax_empty_launches_nothing():
+    assert tg.tg_row_softmax(None, None, 0, 64, tg.TG_DTYPE_F16, 1.0, None) == tg.TG_OK
+    assert tg.tg_row_softmax(None, None, 64, 0, tg.TG_DTYPE_F32, 1.0, None) == tg.TG_OK
+
+
+def test_stream_wrappers_check_before_launch():
+    import torch
+    a = torch.zeros(16, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        tg.vector_add(a, a)  # CPU tensors are refused
+    with pytest.raises(TypeError):
+        tg.vector_add(a.double(), a.double())
+    with pytest.raises(ValueError):
+        tg.row_softmax(a.reshape(4, 4))
+    with pytest.raises(TypeError):
+        tg.row_softmax(a.reshape(4, 4).to(torch.int32))

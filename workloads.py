@@ -15,6 +15,9 @@ Recipe (the same for every workload):
 Sampled comparison positions come from ``torch.randperm(M*N)`` under their own
 seed (without replacement), then ``(i, j) = (idx // N, idx % N)``.
 
+The two bandwidth-bound kernels (vector addition, standalone row softmax) use
+the same ``draw`` on their own seeds (``STREAM_WORKLOADS``).
+
 The TileLang pages measure on synthetic matrices only (no dataset or public
 benchmark suite is involved), so these stand in for nothing external.
 """
@@ -117,3 +120,52 @@ def sample_positions(M: int, N: int, count: int, seed: int):
 def random_matrix(shape, seed: int, dtype: str, dist: str = "normal", scale: float = 1.0) -> torch.Tensor:
     """Generic seeded operand for parity sweeps at arbitrary shapes."""
     return draw(shape, seed, dist, scale, dtype)
+
+
+# ---- the bandwidth-bound kernels ---------------------------------------------
+
+ELEMENT_BYTES = {"f16": 2, "bf16": 2, "f32": 4}
+
+
+@dataclass(frozen=True)
+class StreamWorkload:
+    name: str
+    kind: str               # "vector_add" (n = rows * cols elements) | "row_softmax" (rows x cols)
+    rows: int
+    cols: int
+    dtype: str              # "f16" | "bf16" | "f32"
+    dist: str
+    scale: float
+    seeds: tuple            # (seed_A or seed_X, seed_B or None, seed_sample)
+    alpha: float = 1.0
+    description: str = field(default="", compare=False)
+
+    @property
+    def n(self) -> int:
+        return self.rows * self.cols
+
+    def min_bytes(self) -> int:
+        """Algorithmic HBM bytes: every input read once, every output written once."""
+        e = ELEMENT_BYTES[self.dtype]
+        if self.kind == "vector_add":
+            return 3 * e * self.n
+        return (e + 4) * self.n  # X in its dtype, Y in fp32
+
+
+STREAM_WORKLOADS = {
+    "V1": StreamWorkload("V1", "vector_add", 1, 1 << 22, "f32", "uniform", 1.0, (601, 602, 603),
+                         description="vector add, 2^22 fp32 U[-1,1] (48 MiB moved: fits the 256 MB MALL)"),
+    "V2": StreamWorkload("V2", "vector_add", 1, 1 << 28, "f32", "uniform", 1.0, (611, 612, 613),
+                         description="vector add, 2^28 fp32 U[-1,1] (3 GiB moved: HBM-resident)"),
+    "S1": StreamWorkload("S1", "row_softmax", 16384, 4096, "f16", "normal", 1.0, (621, None, 623),
+                         description="row softmax, X 16384x4096 fp16 N(0,1), alpha 1, fp32 out"),
+}
+
+
+def make_stream_inputs(w: StreamWorkload):
+    """(A, B) for a vector add (flat CPU tensors of n elements), or (X, None) for a
+    row softmax (rows x cols)."""
+    sa, sb, _ = w.seeds
+    if w.kind == "vector_add":
+        return draw((w.n,), sa, w.dist, w.scale, w.dtype), draw((w.n,), sb, w.dist, w.scale, w.dtype)
+    return draw((w.rows, w.cols), sa, w.dist, w.scale, w.dtype), None
