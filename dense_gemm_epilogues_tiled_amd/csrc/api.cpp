@@ -251,6 +251,7 @@ int tg_vector_add(const void* A, const void* B, void* C, int64_t n, int dtype, v
   if (n < 0) return TG_ERR_INVALID_ARG;
   const VectorAddFn fn = vector_add_launcher(dtype);
   if (!fn) return TG_ERR_INVALID_ARG;
+  if (n > (int64_t(1) << 36)) return TG_ERR_UNSUPPORTED;  // keeps the one-vector-per-thread grid < 2^31
   if (n == 0) return TG_OK;
   if (!A || !B || !C) return TG_ERR_INVALID_ARG;
   if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return TG_ERR_MISALIGNED;

@@ -188,10 +188,11 @@ int tg_gemm_query_config(int64_t M, int64_t N, int64_t K, int dtype, int epilogu
  *  Layout  three contiguous vectors of n elements, device memory owned by the
  *          caller, 16-byte aligned.  C may be A or B (in place) but must not
  *          partly overlap either.
- *  n       any n >= 0 (no multiple required); n == 0 launches nothing.
+ *  n       0 <= n <= 2^36 (no multiple required); n == 0 launches nothing.
  *  Errors  NULL pointer with n > 0, negative n or unknown dtype:
- *          TG_ERR_INVALID_ARG; misaligned pointer: TG_ERR_MISALIGNED; a
- *          rejected launch: TG_ERR_HIP.  One kernel is enqueued on `stream`.
+ *          TG_ERR_INVALID_ARG; n > 2^36: TG_ERR_UNSUPPORTED; misaligned
+ *          pointer: TG_ERR_MISALIGNED; a rejected launch: TG_ERR_HIP.  One
+ *          kernel is enqueued on `stream`.
  */
 int tg_vector_add(const void* A, const void* B, void* C, int64_t n, int dtype, void* stream);
 

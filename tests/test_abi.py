@@ -186,6 +186,7 @@ def test_torch_wrapper_checks_before_launch():
 
 @pytest.mark.parametrize("args,expect", [
     (dict(n=-1), tg.TG_ERR_INVALID_ARG),
+    (dict(n=(1 << 36) + 1), tg.TG_ERR_UNSUPPORTED),
     (dict(dtype=3), tg.TG_ERR_INVALID_ARG),
     (dict(dtype=-1), tg.TG_ERR_INVALID_ARG),
     (dict(A=0), tg.TG_ERR_INVALID_ARG),
