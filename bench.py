@@ -38,18 +38,28 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6}
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "C3"
-KERNEL_SOURCES = ["dense_gemm_epilogues_tiled_amd/csrc/gemm.hip", "dense_gemm_epilogues_tiled_amd/csrc/device.hpp",
-                  "dense_gemm_epilogues_tiled_amd/csrc/softmax.hip",
-                  "dense_gemm_epilogues_tiled_amd/csrc/config_table.inc"]
+_CSRC = "dense_gemm_epilogues_tiled_amd/csrc/"
+# The sources each workload's kernel is built from: counter readings taken on
+# other sources are stale.
+KERNEL_SOURCES = {
+    "gemm": [_CSRC + "gemm.hip", _CSRC + "gemm_common.hpp", _CSRC + "device.hpp", _CSRC + "softmax.hip",
+             _CSRC + "config_table.inc"],
+    "stream": [_CSRC + "stream.hip", _CSRC + "device.hpp"],
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha() -> str:
+def kernel_family(workload: str) -> str:
+    import workloads
+    return "stream" if workload in workloads.STREAM_WORKLOADS else "gemm"
+
+
+def kernel_source_sha(family: str = "gemm") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -63,7 +73,7 @@ def measured_traffic(workload: str):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("kernel_source_sha") != kernel_source_sha():
+    if d.get("kernel_source_sha") != kernel_source_sha(kernel_family(workload)):
         return None
     return d.get("bytes_per_launch")
 
@@ -123,7 +133,7 @@ def cpu_baseline(w, A, B, bias):
             "seconds": dt, "cpu_model": cpu_model}
 
 
-def bandwidth_table(dev, stream) -> dict:
+def bandwidth_table(dev, stream, names=None, steps=None, warmup: int = 10) -> dict:
     """The two bandwidth-bound kernels (vector addition and the standalone row
     softmax) on their seeded workloads: algorithmic bytes (inputs read once,
     outputs written once) per event-timed launch, against the HBM peak."""
@@ -133,6 +143,8 @@ def bandwidth_table(dev, stream) -> dict:
     import workloads
     table = {}
     for name, w in workloads.STREAM_WORKLOADS.items():
+        if names is not None and name not in names:
+            continue
         try:
             a, b = workloads.make_stream_inputs(w)
             ad = a.to(dev)
@@ -147,13 +159,14 @@ def bandwidth_table(dev, stream) -> dict:
 
                 def launch(ad=ad, w=w, out=out):
                     tg.row_softmax(ad, alpha=w.alpha, out=out)
-            n = 20 if w.min_bytes() > (1 << 30) else 100
-            wall, ev = time_launches(launch, n, 10, stream)
+            n = steps or (20 if w.min_bytes() > (1 << 30) else 100)
+            wall, ev = time_launches(launch, n, warmup, stream)
             gbs = w.min_bytes() / (ev * 1e-3) / 1e9
             table[name] = {"kernel": "vector_add_kernel" if w.kind == "vector_add" else "row_softmax_kernel",
                            "workload": w.description, "us": round(ev * 1e3, 3), "us_wall": round(wall * 1e3, 3),
                            "algorithmic_bytes": w.min_bytes(), "GB/s": round(gbs, 1),
-                           "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2)}
+                           "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+                           "traffic": measured_traffic(name)}
             log(f"  {name}: {table[name]}")
             del a, b, ad, bd, out
         except Exception as e:  # keep going: one failing workload must not hide the others
@@ -169,7 +182,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2000,
                     help="untimed launches before the timed region (about 50 ms at the headline shape, "
                          "enough for the GPU clocks to settle)")
-    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--workload", default=HEADLINE,
+                    help="GEMM workload to time (default: the headline); a bandwidth workload name (V1, V2, S1) "
+                         "times that kernel alone and prints its entry (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-table", action="store_true", help="skip timing the other workloads")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -208,6 +223,12 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"copy calibration: 3 copies of {args.copy_calibration} MiB")
         del src, dst
+
+    if args.workload in workloads.STREAM_WORKLOADS:
+        # one bandwidth-bound kernel alone (for profiling runs): its table entry
+        t = bandwidth_table(dev, stream, [args.workload], args.steps, args.warmup)
+        print(json.dumps({"workload": args.workload, **t[args.workload]}), flush=True)
+        return 0 if "status" not in t[args.workload] else 1
 
     w = workloads.WORKLOADS[args.workload]
     A, B, bias, Ad, Bd, bd = prepare(w, dev)
