@@ -1,5 +1,5 @@
-"""CPU oracle for Y = epilogue(alpha * A.B + bias) and the tutorial's vector
-addition and row softmax -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for Y = epilogue(alpha * A.B + bias), the tutorial's vector
+addition and row softmax, and attention forward -- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The GPU library never calls it and
@@ -22,6 +22,12 @@ Steps: decode every fp16/bf16 input exactly to fp64; ``acc = sum_k a_ik b_kj``
 in k order with one fp64 accumulator; ``x = alpha*acc + bias_j`` (bias indexed
 by column, broadcast over rows); then none / ReLU ``max(x, 0)`` /
 GELU ``0.5 x (1 + erf(x / sqrt 2))`` / row softmax ``exp(x - max) / sum``.
+
+Attention (what the tutorial's FlashAttention forward computes, section
+"Softmax por linha e FlashAttention" and the other pages' FlashAttention
+paragraphs): per query row, ``s_j = scale * q . k_j`` over all keys (causal:
+keys j <= i), softmax over j, ``o = sum_j p_j v_j``; the plain definition, not
+the online reformulation.  Pins in ``tests/test_oracle_attention.py``.
 
 Pins: every function here is checked in ``tests/test_oracle.py`` against
 closed forms, exact rational arithmetic, library routines and textbook
@@ -90,6 +96,11 @@ def _load():
     lib.oracle_vector_add.restype = ci
     lib.oracle_softmax.argtypes = [vp, f64p, i64, i64, ci, ctypes.c_double, ci]
     lib.oracle_softmax.restype = ci
+    lib.oracle_attention_rows.argtypes = [u16p, u16p, u16p, f64p, i64, i64, i64, i64, ci, ci, ctypes.c_double,
+                                          i64p, i64, ci]
+    lib.oracle_attention_rows.restype = ci
+    lib.oracle_attention.argtypes = [u16p, u16p, u16p, f64p, i64, i64, i64, i64, ci, ci, ctypes.c_double, ci]
+    lib.oracle_attention.restype = ci
     _lib = lib
     return lib
 
@@ -238,3 +249,41 @@ def softmax(X, rows: int, cols: int, dtype: str, alpha: float = 1.0, threads: in
                               threads or default_threads()) != 0:
         raise ValueError("oracle_softmax rejected its arguments")
     return y
+
+
+def _attention_args(Q, K, V, B, H, N, D):
+    q, k, v = _bits(Q).ravel(), _bits(K).ravel(), _bits(V).ravel()
+    if not (q.size == k.size == v.size == B * H * N * D):
+        raise ValueError("Q, K, V must each hold B*H*N*D elements")
+    return q, k, v
+
+
+def attention(Q, K, V, B: int, H: int, N: int, D: int, dtype: str, causal: bool = False,
+              scale: float | None = None, threads: int | None = None) -> np.ndarray:
+    """O = softmax(scale * Q K^T [causal mask]) V per (batch, head); [B][H][N][D]
+    row-major inputs, fp64 output of shape (B, H, N, D).  scale defaults to 1/sqrt(D)."""
+    q, k, v = _attention_args(Q, K, V, B, H, N, D)
+    o = np.empty((B, H, N, D), dtype=np.float64)
+    sc = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    rc = _load().oracle_attention(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
+                                  _ptr(o, ctypes.c_double), B, H, N, D, DTYPES[dtype], int(bool(causal)), sc,
+                                  threads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle_attention rejected its arguments ({rc})")
+    return o
+
+
+def attention_rows(Q, K, V, rows, B: int, H: int, N: int, D: int, dtype: str, causal: bool = False,
+                   scale: float | None = None, threads: int | None = None) -> np.ndarray:
+    """The output rows O[r] for flat query rows r = (b*H + h)*N + i; shape (len(rows), D)."""
+    q, k, v = _attention_args(Q, K, V, B, H, N, D)
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    o = np.empty((r.size, D), dtype=np.float64)
+    sc = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    rc = _load().oracle_attention_rows(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                                       _ptr(v, ctypes.c_uint16), _ptr(o, ctypes.c_double), B, H, N, D,
+                                       DTYPES[dtype], int(bool(causal)), sc, _ptr(r, ctypes.c_int64), r.size,
+                                       threads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle_attention_rows rejected its arguments ({rc})")
+    return o

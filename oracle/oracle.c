@@ -374,3 +374,74 @@ int oracle_softmax(const void* X, double* Y, int64_t rows, int64_t cols, int dty
   }
   return 0;
 }
+
+/* =========================================================================
+ * Attention forward (TEST INFRASTRUCTURE ONLY): the exact result that the
+ * tutorial's FlashAttention kernel computes tile by tile with an online
+ * softmax ("TileLang: Criando Kernels ..." (noticiai.com.br), section
+ * "Softmax por linha e FlashAttention"; the edgex.exchange page's paragraph
+ * on the fused FlashAttention forward, causal and non-causal; spaxe.top,
+ * FlashAttention paragraph).  The online rescaling there is an exact
+ * reformulation, so the reference is the plain definition, written out:
+ *
+ *   for batch b, head h, query i (Q, K, V, O all [B][H][N][D] row-major):
+ *     s_j  = scale * sum_d Q[b,h,i,d] K[b,h,j,d]     for j in J(i)
+ *     J(i) = {0 .. N-1}, or {0 .. i} when causal (key j may not follow query i)
+ *     p_j  = exp(s_j - max s) / sum_j' exp(s_j' - max s)
+ *     O[b,h,i,d] = sum_{j in J(i)} p_j V[b,h,j,d]
+ *
+ * Inputs fp16 / bf16 (dtype 0 / 1) decoded exactly; every sum in fp64, in
+ * index order; O returned in fp64, unrounded.  `rows` lists the flat query
+ * rows r = (b*H + h)*N + i to compute; O receives nrows x D values.
+ * ========================================================================= */
+int oracle_attention_rows(const uint16_t* Q, const uint16_t* K, const uint16_t* V, double* O, int64_t B,
+                          int64_t H, int64_t N, int64_t D, int dtype, int causal, double scale,
+                          const int64_t* rows, int64_t nrows, int nthreads) {
+  if (B < 0 || H < 0 || N < 0 || D < 1 || nrows < 0) return -1;
+  if (dtype != OR_DTYPE_F16 && dtype != OR_DTYPE_BF16) return -1;
+  if (causal != 0 && causal != 1) return -1;
+  for (int64_t t = 0; t < nrows; ++t)
+    if (rows[t] < 0 || rows[t] >= B * H * N) return -1;
+  set_threads(nthreads);
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t t = 0; t < nrows; ++t) {
+    const int64_t bh = rows[t] / N, i = rows[t] % N;
+    const uint16_t* q = Q + rows[t] * D;
+    const uint16_t* k = K + bh * N * D;
+    const uint16_t* v = V + bh * N * D;
+    const int64_t nj = causal ? i + 1 : N;
+    double* s = (double*)malloc((size_t)nj * sizeof(double));
+    if (!s) {
+      bad = 1;
+      continue;
+    }
+    for (int64_t j = 0; j < nj; ++j) {
+      double acc = 0.0;
+      for (int64_t d = 0; d < D; ++d) acc += decode(q[d], dtype) * decode(k[j * D + d], dtype);
+      s[j] = scale * acc;
+    }
+    softmax_row(s, nj);
+    double* o = O + t * D;
+    for (int64_t d = 0; d < D; ++d) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < nj; ++j) acc += s[j] * decode(v[j * D + d], dtype);
+      o[d] = acc;
+    }
+    free(s);
+  }
+  return bad ? -2 : 0;
+}
+
+/* Every query row: O is B x H x N x D. */
+int oracle_attention(const uint16_t* Q, const uint16_t* K, const uint16_t* V, double* O, int64_t B, int64_t H,
+                     int64_t N, int64_t D, int dtype, int causal, double scale, int nthreads) {
+  if (B < 0 || H < 0 || N < 0) return -1;
+  const int64_t total = B * H * N;
+  int64_t* rows = (int64_t*)malloc((size_t)(total > 0 ? total : 1) * sizeof(int64_t));
+  if (!rows) return -2;
+  for (int64_t r = 0; r < total; ++r) rows[r] = r;
+  const int rc = oracle_attention_rows(Q, K, V, O, B, H, N, D, dtype, causal, scale, rows, total, nthreads);
+  free(rows);
+  return rc;
+}
