@@ -45,6 +45,7 @@ KERNEL_SOURCES = {
     "gemm": [_CSRC + "gemm.hip", _CSRC + "gemm_common.hpp", _CSRC + "device.hpp", _CSRC + "softmax.hip",
              _CSRC + "config_table.inc"],
     "stream": [_CSRC + "stream.hip", _CSRC + "device.hpp"],
+    "attention": [_CSRC + "attention.hip", _CSRC + "device.hpp"],
 }
 
 
@@ -54,7 +55,9 @@ def log(*a):
 
 def kernel_family(workload: str) -> str:
     import workloads
-    return "stream" if workload in workloads.STREAM_WORKLOADS else "gemm"
+    if workload in workloads.STREAM_WORKLOADS:
+        return "stream"
+    return "attention" if workload in workloads.ATTN_WORKLOADS else "gemm"
 
 
 def kernel_source_sha(family: str = "gemm") -> str:
@@ -175,6 +178,37 @@ def bandwidth_table(dev, stream, names=None, steps=None, warmup: int = 10) -> di
     return table
 
 
+def attention_table(dev, stream, names=None, steps=None, warmup: int = 5) -> dict:
+    """FlashAttention forward on its seeded workloads: 4 D FLOPs per visible
+    (query, key) pair per event-timed launch, against the MFMA peak."""
+    import torch
+
+    import dense_gemm_epilogues_tiled_amd as tg
+    import workloads
+    table = {}
+    for name, w in workloads.ATTN_WORKLOADS.items():
+        if names is not None and name not in names:
+            continue
+        try:
+            q, k, v = (t.to(dev) for t in workloads.make_attention_inputs(w))
+            out = torch.empty_like(q)
+
+            def launch(q=q, k=k, v=v, w=w, out=out):
+                tg.attention(q, k, v, causal=w.causal, scale=w.scale, out=out)
+            wall, ev = time_launches(launch, steps or 20, warmup, stream)
+            tf = w.flops / (ev * 1e-3) / 1e12
+            table[name] = {"kernel": "attention_fwd_kernel", "workload": w.description, "us": round(ev * 1e3, 3),
+                           "us_wall": round(wall * 1e3, 3), "algorithmic_flops": w.flops, "TFLOP/s": round(tf, 1),
+                           "pct_mfma_peak": round(100 * tf / PEAK_TFLOPS[w.dtype], 2),
+                           "traffic": measured_traffic(name)}
+            log(f"  {name}: {table[name]}")
+            del q, k, v, out
+        except Exception as e:  # keep going: one failing workload must not hide the others
+            table[name] = {"status": f"error: {e}"}
+            log(f"  {name}: error {e}")
+    return table
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,8 +217,8 @@ def main() -> int:
                     help="untimed launches before the timed region (about 50 ms at the headline shape, "
                          "enough for the GPU clocks to settle)")
     ap.add_argument("--workload", default=HEADLINE,
-                    help="GEMM workload to time (default: the headline); a bandwidth workload name (V1, V2, S1) "
-                         "times that kernel alone and prints its entry (for profiling runs)")
+                    help="GEMM workload to time (default: the headline); a bandwidth (V1, V2, S1) or attention "
+                         "(A1, A2) workload name times that kernel alone and prints its entry (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-table", action="store_true", help="skip timing the other workloads")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -227,6 +261,12 @@ def main() -> int:
     if args.workload in workloads.STREAM_WORKLOADS:
         # one bandwidth-bound kernel alone (for profiling runs): its table entry
         t = bandwidth_table(dev, stream, [args.workload], args.steps, args.warmup)
+        print(json.dumps({"workload": args.workload, **t[args.workload]}), flush=True)
+        return 0 if "status" not in t[args.workload] else 1
+
+    if args.workload in workloads.ATTN_WORKLOADS:
+        # the attention forward alone (for profiling runs): its table entry
+        t = attention_table(dev, stream, [args.workload], args.steps, args.warmup)
         print(json.dumps({"workload": args.workload, **t[args.workload]}), flush=True)
         return 0 if "status" not in t[args.workload] else 1
 
@@ -297,6 +337,7 @@ def main() -> int:
                 log(f"  {name}: error {e}")
         result["workloads"] = table
         result["bandwidth"] = bandwidth_table(dev, stream)
+        result["attention"] = attention_table(dev, stream)
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the same workload ...")

@@ -45,6 +45,7 @@ TG_KERNEL_GEMM_SOFTMAX = 1
 
 TG_SOFTMAX_MAX_N = 2048
 TG_ROW_SOFTMAX_MAX_ROW_BYTES = 16384
+TG_ATTN_MAX_SEQ = 1 << 20
 
 EPILOGUES = {
     "none": TG_EPI_NONE, "bias": TG_EPI_BIAS, "relu": TG_EPI_BIAS_RELU, "bias_relu": TG_EPI_BIAS_RELU,
@@ -84,6 +85,9 @@ _SIGNATURES = {
                                      ctypes.c_void_p]),
     "tg_row_softmax": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                       ctypes.c_float, ctypes.c_void_p]),
+    "tg_attention_fwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
     "tg_num_configs": (ctypes.c_int, []),
     "tg_get_config": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(tg_tile_config)]),
     "tg_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -143,6 +147,11 @@ def tg_vector_add(A: int | None, B: int | None, C: int | None, n: int, dtype: in
 def tg_row_softmax(X: int | None, Y: int | None, rows: int, cols: int, dtype: int, alpha: float,
                    stream: int | None) -> int:
     return load().tg_row_softmax(X, Y, rows, cols, dtype, alpha, stream)
+
+
+def tg_attention_fwd(Q: int | None, K: int | None, V: int | None, O: int | None, batch: int, heads: int,
+                     seq_len: int, head_dim: int, dtype: int, causal: int, scale: float, stream: int | None) -> int:
+    return load().tg_attention_fwd(Q, K, V, O, batch, heads, seq_len, head_dim, dtype, causal, scale, stream)
 
 
 def tg_num_configs() -> int:
@@ -252,6 +261,35 @@ def row_softmax(X: torch.Tensor, alpha: float = 1.0, out: torch.Tensor | None = 
                         stream if stream is not None else _stream_handle(X.device))
     if rc != TG_OK:
         raise TgError(rc, "tg_row_softmax")
+    return out
+
+
+def attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, causal: bool = False, scale: float | None = None,
+              out: torch.Tensor | None = None, stream: int | None = None) -> torch.Tensor:
+    """FlashAttention forward through tg_attention_fwd: O = softmax(scale Q K^T [causal]) V.
+
+    Q, K, V: (batch, heads, seq_len, head_dim) contiguous fp16 or bf16 on one GPU
+    (head_dim 128); scale defaults to 1/sqrt(head_dim).  O has Q's shape and dtype.
+    """
+    if Q.dtype not in DTYPES or K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise TypeError("Q, K and V must share one dtype, float16 or bfloat16")
+    if not (Q.is_cuda and K.is_cuda and V.is_cuda) or not (Q.device == K.device == V.device):
+        raise ValueError("Q, K and V must be on one GPU")
+    if Q.dim() != 4 or K.shape != Q.shape or V.shape != Q.shape:
+        raise ValueError("Q, K and V must be 4-D (batch, heads, seq_len, head_dim) of one shape")
+    for name, t in (("Q", Q), ("K", K), ("V", V)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, H, N, D = Q.shape
+    if out is None:
+        out = torch.empty_like(Q)
+    elif out.shape != Q.shape or out.dtype != Q.dtype or not out.is_contiguous() or out.device != Q.device:
+        raise ValueError("out has the wrong shape, dtype, layout or device")
+    sc = float(D) ** -0.5 if scale is None else float(scale)
+    rc = tg_attention_fwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(), out.data_ptr(), B, H, N, D, DTYPES[Q.dtype],
+                          int(bool(causal)), sc, stream if stream is not None else _stream_handle(Q.device))
+    if rc != TG_OK:
+        raise TgError(rc, "tg_attention_fwd")
     return out
 
 

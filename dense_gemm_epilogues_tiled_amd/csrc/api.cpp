@@ -9,6 +9,7 @@
 // to a rule that keeps every compute unit busy with the largest tile.
 
 #include <hip/hip_runtime_api.h>
+#include <math.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -276,6 +277,39 @@ int tg_row_softmax(const void* X, float* Y, int64_t rows, int64_t cols, int dtyp
   if (log_enabled())
     fprintf(stderr, "tg: row_softmax rows=%lld cols=%lld dtype=%d -> %s\n", (long long)rows, (long long)cols, dtype,
             hipGetErrorString(err));
+  return err == hipSuccess ? TG_OK : TG_ERR_HIP;
+}
+
+int tg_attention_fwd(const void* Q, const void* K, const void* V, void* O, int64_t batch, int64_t heads,
+                     int64_t seq_len, int64_t head_dim, int dtype, int causal, float scale, void* stream) {
+  if (batch < 0 || heads < 0 || seq_len < 0 || head_dim < 0) return TG_ERR_INVALID_ARG;
+  if (dtype != TG_DTYPE_F16 && dtype != TG_DTYPE_BF16) return TG_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return TG_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return TG_ERR_INVALID_ARG;
+  const AttnFn fn = attention_launcher(dtype, (int)(head_dim > 1024 ? 0 : head_dim), causal);
+  if (!fn || seq_len > TG_ATTN_MAX_SEQ) return TG_ERR_UNSUPPORTED;
+  const int64_t bm = attention_block_queries();
+  const int64_t q_blocks = cdiv(seq_len, bm);
+  if (heads > 0 && batch > ((int64_t(1) << 31) - 1) / heads) return TG_ERR_UNSUPPORTED;
+  const int64_t groups = batch * heads * q_blocks;
+  if (groups >= (int64_t(1) << 31)) return TG_ERR_UNSUPPORTED;
+  if (groups == 0) return TG_OK;
+  if (!Q || !K || !V || !O) return TG_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return TG_ERR_MISALIGNED;
+  AttnParams p;
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.O = O;
+  p.N = (int)seq_len;
+  p.q_blocks = (int)q_blocks;
+  p.groups = (int)groups;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const hipError_t err = fn(p, static_cast<hipStream_t>(stream));
+  if (log_enabled())
+    fprintf(stderr, "tg: attention_fwd B=%lld H=%lld N=%lld D=%lld dtype=%d causal=%d grid=%lld -> %s\n",
+            (long long)batch, (long long)heads, (long long)seq_len, (long long)head_dim, dtype, causal,
+            (long long)groups, hipGetErrorString(err));
   return err == hipSuccess ? TG_OK : TG_ERR_HIP;
 }
 

@@ -1,0 +1,297 @@
+// attention.hip -- FlashAttention forward for gfx950 (fp16 / bf16, head dim 128,
+// causal or not):
+//
+//     O = softmax(scale * Q K^T [key j <= query i when causal]) V   per (batch, head)
+//
+// The tutorial's capstone ("TileLang: Criando Kernels ..." (noticiai.com.br),
+// section "Softmax por linha e FlashAttention"; the edgex.exchange page's
+// FlashAttention paragraph; spaxe.top, FlashAttention paragraph): query, key
+// and value tiles are processed without writing the score matrix to memory;
+// an online softmax keeps a running maximum and a running sum per query and
+// rescales the partial output whenever the maximum grows; both products run
+// on the matrix units.
+//
+// gfx950 design
+// -------------
+// A workgroup of 4 waves owns 128 consecutive queries of one (batch, head):
+// 32 per wave, held in registers as MFMA operands for the whole kernel.  Key
+// and value blocks of 64 rows stream through a two-stage LDS ring, copied
+// HBM/L2 -> LDS with the direct 16-byte-per-lane copies (no VGPR staging);
+// keys past the sequence end are zero-filled by the buffer range check.
+//
+// Each wave computes the transposed score tile S^T = K Q^T (64 keys x 32
+// queries) with v_mfma_f32_16x16x32: lane l then holds, for query l % 16,
+// four consecutive keys 4 (l / 16) .. +3 of each 16-key tile.  Those are
+// exactly the values the second product needs from the lane, in that order:
+// O^T += V^T P^T takes P^T as its B operand with the MFMA's 32-deep k axis
+// mapped to keys {4g .. 4g+3} of one 16-key tile and {4g .. 4g+3} of the next
+// (g = l / 16), and V^T as its A operand read with ds_read_b64_tr_b16 using
+// the same key order (an MFMA sums over k in any order, as long as both
+// operands agree).  So P never leaves the registers and is never shuffled;
+// per-query statistics need only the 4 lanes that share a query (xor 16, 32).
+// The online softmax works in base 2 (exp2 on scale * log2 e * score), keeps
+// per-lane partial sums (the 4 lanes of a query are rescaled by the same
+// factors) and reduces them once at the end.
+
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace tg {
+
+namespace {
+
+constexpr int kAttnWaves = 4;
+constexpr int kAttnQW = 32;                      // queries per wave
+constexpr int kAttnBM = kAttnWaves * kAttnQW;    // queries per workgroup
+constexpr int kAttnBN = 64;                      // keys per block
+
+template <int D>
+struct AttnShape {
+  static_assert(D == 128, "head dim 128 (the n-contiguous V swizzle needs 128 columns)");
+  static constexpr int KBYTES = kAttnBN * D * 2;           // one K block in LDS
+  static constexpr int VBYTES = kAttnBN * D * 2;           // one V block in LDS
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int LDS = 2 * STAGE;                    // two-stage ring
+  static constexpr int KCOPIES = KBYTES / 1024 / kAttnWaves;  // 1 KB copies per wave per block
+  static constexpr int VCOPIES = VBYTES / 1024 / kAttnWaves;
+  static_assert(KCOPIES * 1024 * kAttnWaves == KBYTES && VCOPIES * 1024 * kAttnWaves == VBYTES, "1 KB pieces");
+};
+
+// Per-lane source offsets (bytes from the block's first key row) of this
+// wave's copies, chosen so that the LDS image of a block is the swizzled
+// layout the fragment reads expect: K rows k-contiguous (kc_off), V rows
+// n-contiguous (nc_off).
+template <int D>
+struct AttnCopies {
+  int k_off[AttnShape<D>::KCOPIES], k_row[AttnShape<D>::KCOPIES];
+  int v_off[AttnShape<D>::VCOPIES], v_row[AttnShape<D>::VCOPIES];
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+    constexpr int KCH = D / 8;
+#pragma unroll
+    for (int j = 0; j < AttnShape<D>::KCOPIES; ++j) {
+      const int pos = 1024 * (wave + kAttnWaves * j) + 16 * lane;
+      const int row = pos / (D * 2);
+      const int slot = (pos % (D * 2)) / 16;
+      const int chunk = slot ^ ((row / (16 / KCH)) % KCH);
+      k_off[j] = row * D * 2 + chunk * 16;
+      k_row[j] = row;
+    }
+#pragma unroll
+    for (int j = 0; j < AttnShape<D>::VCOPIES; ++j) {
+      const int pos = 1024 * (wave + kAttnWaves * j) + 16 * lane;
+      const int row = pos / (D * 2);
+      const int slot = (pos % (D * 2)) / 16;
+      const int chunk = (((slot >> 1) ^ nc_swz(row)) << 1) | (slot & 1);
+      v_off[j] = row * D * 2 + chunk * 16;
+      v_row[j] = row;
+    }
+  }
+
+  // Copy key / value block starting at key kb into the stage at LDS byte
+  // address `stage`; rows at or past n read zeros.
+  __device__ __forceinline__ void issue(int wave, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int kb, int n,
+                                        uint32_t stage) const {
+    const int rows_left = n - kb;
+    const int base = kb * D * 2;
+#pragma unroll
+    for (int j = 0; j < AttnShape<D>::KCOPIES; ++j)
+      dma16(kr, stage + 1024 * (wave + kAttnWaves * j), k_row[j] < rows_left ? base + k_off[j] : kOOB);
+#pragma unroll
+    for (int j = 0; j < AttnShape<D>::VCOPIES; ++j)
+      dma16(vr, stage + AttnShape<D>::KBYTES + 1024 * (wave + kAttnWaves * j),
+            v_row[j] < rows_left ? base + v_off[j] : kOOB);
+  }
+};
+
+// Buffer resource over one head's N x D block (range = its bytes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, int64_t head, int n, int d) {
+  const unsigned char* p = static_cast<const unsigned char*>(base) + head * (int64_t)n * d * 2;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(p), (short)0, n * d * 2, 0x00020000);
+}
+
+}  // namespace
+
+template <int D, class DT, bool CAUSAL>
+__global__ __launch_bounds__(256) void attention_fwd_kernel(AttnParams p) {
+  using S = AttnShape<D>;
+  constexpr int KT = kAttnBN / 16;  // 16-key tiles per block
+  constexpr int QT = kAttnQW / 16;  // 16-query tiles per wave
+  constexpr int DK = D / 32;        // 32-deep slices of the QK^T product
+  constexpr int NDT = D / 16;       // 16-row tiles of O^T
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[S::LDS];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the copies' LDS base goes to m0
+  const int fr = lane & 15, fk = lane >> 4;
+
+  // workgroup -> (head, query block): each XCD takes a contiguous range of
+  // heads (workgroups are dealt to the 8 XCDs round robin), so a head's K / V
+  // stay in one L2; within a head the query blocks run last-to-first, so the
+  // causal kernel starts its longest blocks first.
+  const int groups = gridDim.x;
+  int lin = blockIdx.x;
+  if ((groups & 7) == 0) lin = (lin & 7) * (groups >> 3) + (lin >> 3);
+  const int64_t head = lin / p.q_blocks;
+  const int qb = p.q_blocks - 1 - lin % p.q_blocks;
+  const int n = p.N;
+  const int q0 = qb * kAttnBM;
+  const int q0w = q0 + wave * kAttnQW;
+
+  const __amdgpu_buffer_rsrc_t qr = head_rsrc(p.Q, head, n, D);
+  const __amdgpu_buffer_rsrc_t kr = head_rsrc(p.K, head, n, D);
+  const __amdgpu_buffer_rsrc_t vr = head_rsrc(p.V, head, n, D);
+
+  AttnCopies<D> cp;
+  cp.init(wave, lane);
+  const uint32_t lds0 = lds_addr(smem);
+  const int kend = CAUSAL ? (q0 + kAttnBM < n ? q0 + kAttnBM : n) : n;
+  const int nblk = (kend + kAttnBN - 1) / kAttnBN;
+  cp.issue(wave, kr, vr, 0, n, lds0);
+
+  // Q^T fragments (B operand of S^T = K Q^T): query q0w + 16 qt + fr, dims
+  // 32 kk + 8 fk .. +7; queries past n read zeros.
+  u32x4 qf[QT][DK];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk)
+      qf[qt][kk] = buffer_load16(qr, (q0w + 16 * qt + fr) * D * 2 + (32 * kk + 8 * fk) * 2);
+
+  f32x4 o[NDT][QT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[QT], l[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m[qt] = -__builtin_inff();
+    l[qt] = 0.f;
+  }
+  const float sl2 = p.scale_log2;
+
+  wait_vm_barrier<0>();
+  for (int j = 0; j < nblk; ++j) {
+    const uint32_t stage = lds0 + (j & 1) * S::STAGE;
+    if (j + 1 < nblk) cp.issue(wave, kr, vr, (j + 1) * kAttnBN, n, lds0 + ((j + 1) & 1) * S::STAGE);
+    const int kb = j * kAttnBN;
+    // a causal block entirely after this wave's last query adds nothing
+    if (!CAUSAL || kb <= q0w + kAttnQW - 1) {
+      const unsigned char* sK = smem + (j & 1) * S::STAGE;
+      const unsigned char* sV = sK + S::KBYTES;
+
+      // S^T = K Q^T: tile [kt][qt], lane holds query 16 qt + fr, keys 16 kt + 4 fk + r
+      f32x4 st[KT][QT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) st[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < DK; ++kk)
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          const u32x4 a = lds_read16(sK, kc_off<D>(16 * kt + fr, 4 * kk + fk));
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) st[kt][qt] = mfma16x16x32(DT{}, a, qf[qt][kk], st[kt][qt]);
+        }
+
+      // online softmax (base 2) and P^T operands
+      u32x4 pb[QT][KT / 2];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const int query = q0w + 16 * qt + fr;
+        float bm = -__builtin_inff();
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = kb + 16 * kt + 4 * fk + r;
+            const bool ok = key < n && (!CAUSAL || key <= query);
+            const float s = ok ? st[kt][qt][r] * sl2 : -__builtin_inff();
+            st[kt][qt][r] = s;
+            bm = __builtin_fmaxf(bm, s);
+          }
+        bm = __builtin_fmaxf(bm, __shfl_xor(bm, 16));
+        bm = __builtin_fmaxf(bm, __shfl_xor(bm, 32));
+        const float mn = __builtin_fmaxf(m[qt], bm);
+        const float mu = mn == -__builtin_inff() ? 0.f : mn;  // nothing visible yet: keep exp2 finite
+        const float corr = __builtin_amdgcn_exp2f(m[qt] - mu);
+        m[qt] = mn;
+        float ps = 0.f;
+        float pv[KT][4];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pv[kt][r] = __builtin_amdgcn_exp2f(st[kt][qt][r] - mu);
+            ps += pv[kt][r];
+          }
+        l[qt] = l[qt] * corr + ps;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt][qt] *= corr;
+#pragma unroll
+        for (int u = 0; u < KT / 2; ++u)
+          pb[qt][u] = u32x4{pack2(DT{}, pv[2 * u][0], pv[2 * u][1]), pack2(DT{}, pv[2 * u][2], pv[2 * u][3]),
+                            pack2(DT{}, pv[2 * u + 1][0], pv[2 * u + 1][1]),
+                            pack2(DT{}, pv[2 * u + 1][2], pv[2 * u + 1][3])};
+      }
+
+      // O^T += V^T P^T: A operand = V^T rows 16 dt .. +15 (dims), k = keys
+      // {32u + 4 fk .. +3} then {32u + 16 + 4 fk .. +3}, read transposed
+#pragma unroll
+      for (int u = 0; u < KT / 2; ++u)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int chunk = 2 * dt + ((fr & 3) >> 1);
+          const int key = 32 * u + 4 * fk + (fr >> 2);
+          const u32x2 lo = lds_read_tr8(sV, nc_off<D>(key, chunk) + 8 * (fr & 1));
+          const u32x2 hi = lds_read_tr8(sV, nc_off<D>(key + 16, chunk) + 8 * (fr & 1));
+          const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) o[dt][qt] = mfma16x16x32(DT{}, a, pb[qt][u], o[dt][qt]);
+        }
+    }
+    // this wave's copies of block j + 1 have landed and every wave is done
+    // with block j's stage before it is overwritten
+    wait_vm_barrier<0>();
+  }
+
+  // finish: O = O^T / l, lane writes dims 16 dt + 4 fk .. +3 of its query
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float lt = l[qt];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const float inv = 1.0f / lt;
+    const int query = q0w + 16 * qt + fr;
+    if (query < n) {
+      uint16_t* orow = static_cast<uint16_t*>(p.O) + (head * n + query) * (int64_t)D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const f32x4 v = o[dt][qt];
+        *reinterpret_cast<u32x2*>(orow + 16 * dt + 4 * fk) =
+            u32x2{pack2(DT{}, v[0] * inv, v[1] * inv), pack2(DT{}, v[2] * inv, v[3] * inv)};
+      }
+    }
+  }
+}
+
+template <int D, class DT, bool CAUSAL>
+static hipError_t launch_attention(const AttnParams& p, hipStream_t stream) {
+  void* args[] = {const_cast<AttnParams*>(&p)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attention_fwd_kernel<D, DT, CAUSAL>),
+                         dim3((unsigned)p.groups), dim3(256), args, 0, stream);
+}
+
+__host__ AttnFn attention_launcher(int dtype, int head_dim, int causal) {
+  if (head_dim != 128) return nullptr;
+  if (dtype == TG_DTYPE_F16) return causal ? &launch_attention<128, F16, true> : &launch_attention<128, F16, false>;
+  if (dtype == TG_DTYPE_BF16)
+    return causal ? &launch_attention<128, BF16, true> : &launch_attention<128, BF16, false>;
+  return nullptr;
+}
+
+__host__ int attention_block_queries() { return kAttnBM; }
+
+}  // namespace tg

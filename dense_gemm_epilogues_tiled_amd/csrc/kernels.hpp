@@ -1,5 +1,5 @@
 // kernels.hpp -- interface between the host dispatch (api.cpp) and the
-// compiled kernel variants (gemm.hip, softmax.hip, stream.hip).
+// compiled kernel variants (gemm.hip, softmax.hip, stream.hip, attention.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -50,12 +50,28 @@ struct RowSoftmaxParams {
   float alpha;
 };
 
+// Kernel arguments of the attention forward (attention.hip).
+struct AttnParams {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  int N;            // sequence length
+  int q_blocks;     // query blocks per (batch, head)
+  int groups;       // workgroups: batch * heads * q_blocks
+  float scale_log2; // scale * log2(e)
+};
+
 typedef hipError_t (*VectorAddFn)(const VectorAddParams&, hipStream_t);
 typedef hipError_t (*RowSoftmaxFn)(const RowSoftmaxParams&, hipStream_t);
 
-// Launchers for a dtype (and row length); NULL when unsupported.
+typedef hipError_t (*AttnFn)(const AttnParams&, hipStream_t);
+
+// Launchers for a dtype (and row length / head dim); NULL when unsupported.
 VectorAddFn vector_add_launcher(int dtype);
 RowSoftmaxFn row_softmax_launcher(int dtype, int64_t cols);
+AttnFn attention_launcher(int dtype, int head_dim, int causal);
+int attention_block_queries();  // queries per attention workgroup
 
 typedef hipError_t (*GemmLaunchFn)(const GemmParams&, hipStream_t);
 typedef hipError_t (*SoftmaxLaunchFn)(const SoftmaxParams&, hipStream_t);

@@ -219,6 +219,44 @@ int tg_vector_add(const void* A, const void* B, void* C, int64_t n, int dtype, v
  */
 int tg_row_softmax(const void* X, float* Y, int64_t rows, int64_t cols, int dtype, float alpha, void* stream);
 
+/* Longest sequence tg_attention_fwd takes. */
+#define TG_ATTN_MAX_SEQ (1 << 20)
+
+/*
+ * tg_attention_fwd -- FlashAttention forward.  For every batch b and head h:
+ *
+ *     O[b,h] = softmax(scale * Q[b,h] K[b,h]^T) V[b,h]     (softmax over keys)
+ *
+ * and, when causal = 1, key j is visible to query i only if j <= i.
+ *
+ * The tutorial's capstone kernel ("TileLang: Criando Kernels ..."
+ * (noticiai.com.br), section "Softmax por linha e FlashAttention"; the
+ * edgex.exchange page's FlashAttention paragraph, causal and non-causal; the
+ * spaxe.top FlashAttention paragraph): tiles of queries, keys and values are
+ * combined with an online softmax (running max, running sum, rescaling), the
+ * score matrix never reaches memory, and both products run on the matrix
+ * units.
+ *
+ *  dtype   TG_DTYPE_F16 or TG_DTYPE_BF16, for Q, K, V and O alike.  Scores
+ *          and the softmax are fp32; the probabilities are rounded to dtype as
+ *          the matrix units take them for the second product; O is
+ *          accumulated in fp32 and rounded once, to nearest even.
+ *  Layout  Q, K, V, O: [batch][heads][seq_len][head_dim] row-major, packed,
+ *          device memory owned by the caller, 16-byte aligned.  O must not
+ *          overlap Q, K or V.
+ *  Limits  head_dim == 128 (else TG_ERR_UNSUPPORTED); 0 <= seq_len <=
+ *          TG_ATTN_MAX_SEQ; batch, heads >= 0 with batch * heads *
+ *          ceil(seq_len / 128) < 2^31 (else TG_ERR_UNSUPPORTED).
+ *  scale   finite (usually 1 / sqrt(head_dim)); NaN or infinite:
+ *          TG_ERR_INVALID_ARG.
+ *  Degenerate  batch, heads or seq_len zero: nothing is launched, TG_OK.
+ *  Errors  negative sizes, unknown dtype, causal not 0 / 1, NULL pointers:
+ *          TG_ERR_INVALID_ARG; misaligned pointers: TG_ERR_MISALIGNED; a
+ *          rejected launch: TG_ERR_HIP.  One kernel is enqueued on `stream`.
+ */
+int tg_attention_fwd(const void* Q, const void* K, const void* V, void* O, int64_t batch, int64_t heads,
+                     int64_t seq_len, int64_t head_dim, int dtype, int causal, float scale, void* stream);
+
 /* Number of compiled tile configurations (ids 0 .. n-1). */
 int tg_num_configs(void);
 

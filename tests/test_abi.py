@@ -29,7 +29,7 @@ def _declared_functions():
 def test_header_declares_expected_entry_points():
     names = _declared_functions()
     for n in ("tg_gemm", "tg_gemm_ex", "tg_gemm_query_config", "tg_num_configs", "tg_get_config",
-              "tg_status_string", "tg_version", "tg_vector_add", "tg_row_softmax"):
+              "tg_status_string", "tg_version", "tg_vector_add", "tg_row_softmax", "tg_attention_fwd"):
         assert n in names
 
 
@@ -253,3 +253,53 @@ def test_stream_wrappers_check_before_launch():
         tg.row_softmax(a.reshape(4, 4))
     with pytest.raises(TypeError):
         tg.row_softmax(a.reshape(4, 4).to(torch.int32))
+
+
+# ---- attention forward -------------------------------------------------------------
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(batch=-1), tg.TG_ERR_INVALID_ARG),
+    (dict(heads=-2), tg.TG_ERR_INVALID_ARG),
+    (dict(seq_len=-5), tg.TG_ERR_INVALID_ARG),
+    (dict(head_dim=-128), tg.TG_ERR_INVALID_ARG),
+    (dict(dtype=tg.TG_DTYPE_F32), tg.TG_ERR_INVALID_ARG),
+    (dict(dtype=9), tg.TG_ERR_INVALID_ARG),
+    (dict(causal=2), tg.TG_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), tg.TG_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), tg.TG_ERR_INVALID_ARG),
+    (dict(head_dim=64), tg.TG_ERR_UNSUPPORTED),
+    (dict(head_dim=96), tg.TG_ERR_UNSUPPORTED),
+    (dict(head_dim=1 << 40), tg.TG_ERR_UNSUPPORTED),
+    (dict(seq_len=(1 << 20) + 1), tg.TG_ERR_UNSUPPORTED),
+    (dict(batch=1 << 20, heads=1 << 12), tg.TG_ERR_UNSUPPORTED),   # grid of 2^32 workgroups
+    (dict(batch=1 << 62, heads=4), tg.TG_ERR_UNSUPPORTED),          # product would overflow
+    (dict(Q=0), tg.TG_ERR_INVALID_ARG),
+    (dict(K=0), tg.TG_ERR_INVALID_ARG),
+    (dict(V=0), tg.TG_ERR_INVALID_ARG),
+    (dict(O=0), tg.TG_ERR_INVALID_ARG),
+    (dict(Q=4104), tg.TG_ERR_MISALIGNED),
+    (dict(K=8200), tg.TG_ERR_MISALIGNED),
+    (dict(V=12290), tg.TG_ERR_MISALIGNED),
+    (dict(O=16392), tg.TG_ERR_MISALIGNED),
+])
+def test_attention_rejects_before_any_hip_call(args, expect):
+    base = dict(Q=4096, K=8192, V=12288, O=16384, batch=2, heads=4, seq_len=256, head_dim=128,
+                dtype=tg.TG_DTYPE_F16, causal=0, scale=0.125)
+    base.update(args)
+    assert tg.tg_attention_fwd(base["Q"] or None, base["K"] or None, base["V"] or None, base["O"] or None,
+                               base["batch"], base["heads"], base["seq_len"], base["head_dim"], base["dtype"],
+                               base["causal"], base["scale"], None) == expect
+
+
+def test_attention_empty_launches_nothing():
+    for b, h, n in ((0, 4, 256), (2, 0, 256), (2, 4, 0)):
+        assert tg.tg_attention_fwd(None, None, None, None, b, h, n, 128, tg.TG_DTYPE_BF16, 1, 0.1, None) == tg.TG_OK
+
+
+def test_attention_wrapper_checks_before_launch():
+    import torch
+    q = torch.zeros(1, 2, 8, 128, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        tg.attention(q, q, q)  # CPU tensors are refused
+    with pytest.raises(TypeError):
+        tg.attention(q.float(), q.float(), q.float())

@@ -1,0 +1,100 @@
+"""GPU parity of tg_attention_fwd against the fp64 attention oracle.
+
+The two 4 x 16 x 4096 x 128 fp16 workloads (non-causal and causal) in the
+launch configuration the benchmark times, on 512 seeded query rows each (the
+oracle computes a row from its definition: every visible key); then full
+comparisons over ragged sequence lengths (below, at and across the 128-query
+and 64-key tiles), both dtypes, both masks, several scales and large scores.
+Bound: |g - y| <= 1e-2 + 1e-2 |y| per element and relative Frobenius error
+<= 2e-3 (small shapes: 1.5 x the error of the correctly rounded result when
+that alone exceeds 2e-3).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from _compare import assert_accept, to_f64
+
+tg = pytest.importorskip("dense_gemm_epilogues_tiled_amd")
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TD = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _run(Q, K, V, causal, scale=None):
+    O = tg.attention(Q.to(DEV), K.to(DEV), V.to(DEV), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return O
+
+
+@pytest.mark.parametrize("name", ["A1", "A2"])
+def test_workload_sampled_rows(name):
+    w = workloads.ATTN_WORKLOADS[name]
+    print(f"[parity] {name}: {w.description}", flush=True)
+    Q, K, V = workloads.make_attention_inputs(w)
+    O = _run(Q, K, V, w.causal, w.scale)
+    total = w.B * w.H * w.N
+    g = torch.Generator(device="cpu").manual_seed(w.seeds[3])
+    rows = torch.randperm(total, generator=g)[:512]
+    # the first and last query of the first and last head too
+    rows = torch.cat([rows, torch.tensor([0, w.N - 1, total - w.N, total - 1])]).numpy()
+    y = oracle.attention_rows(Q, K, V, rows, w.B, w.H, w.N, w.D, w.dtype, w.causal, w.scale)
+    got = to_f64(O.reshape(-1, w.D)[torch.from_numpy(rows).to(DEV)])
+    s = assert_accept(got, y, w.dtype, f"{name} sampled rows")
+    print(f"[parity] {name}: {s}", flush=True)
+
+
+_SHAPES = [(1, 1, 1), (1, 2, 63), (1, 1, 64), (2, 1, 65), (1, 2, 128), (1, 1, 129), (2, 3, 200), (1, 2, 333),
+           (1, 1, 1000)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_lengths(dtype, causal):
+    for i, (B, H, N) in enumerate(_SHAPES):
+        print(f"[parity] attention {dtype} causal={causal} B={B} H={H} N={N}", flush=True)
+        Q, K, V = (workloads.random_matrix((B, H, N, 128), 800 + 10 * i + j, dtype) for j in range(3))
+        O = _run(Q, K, V, causal)
+        y = oracle.attention(Q, K, V, B, H, N, 128, dtype, causal)
+        assert_accept(to_f64(O).reshape(-1), y.reshape(-1), dtype, f"{dtype} causal={causal} {B}x{H}x{N}",
+                      small=True)
+
+
+@pytest.mark.parametrize("scale", [0.0, 0.02, 0.3])
+def test_scales(scale):
+    print(f"[parity] attention scale={scale}", flush=True)
+    B, H, N = 1, 2, 300
+    Q, K, V = (workloads.random_matrix((B, H, N, 128), 900 + j, "f16") for j in range(3))
+    for causal in (False, True):
+        O = _run(Q, K, V, causal, scale)
+        y = oracle.attention(Q, K, V, B, H, N, 128, "f16", causal, scale)
+        assert_accept(to_f64(O).reshape(-1), y.reshape(-1), "f16", f"scale={scale} causal={causal}", small=True)
+
+
+def test_large_scores_are_stable():
+    """Scores in the hundreds: exp overflows without the running max."""
+    print("[parity] attention large scores", flush=True)
+    B, H, N = 1, 1, 700
+    Q = workloads.random_matrix((B, H, N, 128), 950, "bf16", "normal", 4.0)
+    K = workloads.random_matrix((B, H, N, 128), 951, "bf16", "normal", 4.0)
+    V = workloads.random_matrix((B, H, N, 128), 952, "bf16")
+    for causal in (False, True):
+        O = _run(Q, K, V, causal, 1.0)
+        y = oracle.attention(Q, K, V, B, H, N, 128, "bf16", causal, 1.0)
+        assert_accept(to_f64(O).reshape(-1), y.reshape(-1), "bf16", f"large causal={causal}", small=True)
+
+
+def test_causal_first_row_is_first_value_row():
+    B, H, N = 2, 2, 257
+    Q, K, V = (workloads.random_matrix((B, H, N, 128), 960 + j, "f16") for j in range(3))
+    O = _run(Q, K, V, True)
+    assert torch.equal(O[:, :, 0].cpu(), V[:, :, 0])  # one visible key: p = 1 exactly
+
+
+def test_empty():
+    z = torch.empty((2, 3, 0, 128), dtype=torch.float16, device=DEV)
+    assert tg.attention(z, z, z).shape == (2, 3, 0, 128)

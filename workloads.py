@@ -169,3 +169,47 @@ def make_stream_inputs(w: StreamWorkload):
     if w.kind == "vector_add":
         return draw((w.n,), sa, w.dist, w.scale, w.dtype), draw((w.n,), sb, w.dist, w.scale, w.dtype)
     return draw((w.rows, w.cols), sa, w.dist, w.scale, w.dtype), None
+
+
+# ---- attention forward -----------------------------------------------------------
+
+@dataclass(frozen=True)
+class AttnWorkload:
+    name: str
+    B: int
+    H: int
+    N: int
+    D: int
+    dtype: str
+    causal: bool
+    seeds: tuple            # (seed_Q, seed_K, seed_V, seed_sample)
+    description: str = field(default="", compare=False)
+
+    @property
+    def scale(self) -> float:
+        """1/sqrt(D) as the fp32 value both sides receive."""
+        return float(torch.tensor(1.0 / math.sqrt(self.D), dtype=torch.float32))
+
+    @property
+    def flops(self) -> int:
+        """4 D FLOPs (two products) per visible (query, key) pair."""
+        pairs = self.N * (self.N + 1) // 2 if self.causal else self.N * self.N
+        return 4 * self.B * self.H * self.D * pairs
+
+    def min_bytes(self) -> int:
+        """Q, K, V read once, O written once."""
+        return 4 * self.B * self.H * self.N * self.D * ELEMENT_BYTES[self.dtype]
+
+
+ATTN_WORKLOADS = {
+    "A1": AttnWorkload("A1", 4, 16, 4096, 128, "f16", False, (701, 702, 703, 704),
+                       description="attention fwd, B=4 H=16 N=4096 D=128 fp16 N(0,1), non-causal, scale 1/sqrt(128)"),
+    "A2": AttnWorkload("A2", 4, 16, 4096, 128, "f16", True, (711, 712, 713, 714),
+                       description="attention fwd, B=4 H=16 N=4096 D=128 fp16 N(0,1), causal, scale 1/sqrt(128)"),
+}
+
+
+def make_attention_inputs(w: AttnWorkload):
+    """(Q, K, V) CPU tensors of shape (B, H, N, D), N(0,1) rounded to the dtype."""
+    shape = (w.B, w.H, w.N, w.D)
+    return tuple(draw(shape, s, "normal", 1.0, w.dtype) for s in w.seeds[:3])
