@@ -261,13 +261,13 @@ def main() -> int:
     if args.workload in workloads.STREAM_WORKLOADS:
         # one bandwidth-bound kernel alone (for profiling runs): its table entry
         t = bandwidth_table(dev, stream, [args.workload], args.steps, args.warmup)
-        print(json.dumps({"workload": args.workload, **t[args.workload]}), flush=True)
+        print(json.dumps({"name": args.workload, **t[args.workload]}), flush=True)
         return 0 if "status" not in t[args.workload] else 1
 
     if args.workload in workloads.ATTN_WORKLOADS:
         # the attention forward alone (for profiling runs): its table entry
         t = attention_table(dev, stream, [args.workload], args.steps, args.warmup)
-        print(json.dumps({"workload": args.workload, **t[args.workload]}), flush=True)
+        print(json.dumps({"name": args.workload, **t[args.workload]}), flush=True)
         return 0 if "status" not in t[args.workload] else 1
 
     w = workloads.WORKLOADS[args.workload]

@@ -304,7 +304,12 @@ int tg_attention_fwd(const void* Q, const void* K, const void* V, void* O, int64
   p.N = (int)seq_len;
   p.q_blocks = (int)q_blocks;
   p.groups = (int)groups;
-  p.scale_log2 = scale * 1.4426950408889634f;
+  // |scale| log2 e, kept strictly positive: a masked score is -inf and
+  // -inf * 0 would be NaN; 2^-100 times any finite score is below 2^-25, whose
+  // exp2 is exactly 1, the same as for a zero scale
+  p.scale_log2 = fabsf(scale) * 1.4426950408889634f;
+  if (!(p.scale_log2 >= 0x1p-100f)) p.scale_log2 = 0x1p-100f;
+  p.negate_q = scale < 0.f ? 1 : 0;
   const hipError_t err = fn(p, static_cast<hipStream_t>(stream));
   if (log_enabled())
     fprintf(stderr, "tg: attention_fwd B=%lld H=%lld N=%lld D=%lld dtype=%d causal=%d grid=%lld -> %s\n",

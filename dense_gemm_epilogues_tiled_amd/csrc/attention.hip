@@ -113,7 +113,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, in
 }  // namespace
 
 template <int D, class DT, bool CAUSAL>
-__global__ __launch_bounds__(256) void attention_fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__(256, 2) void attention_fwd_kernel(AttnParams p) {
   using S = AttnShape<D>;
   constexpr int KT = kAttnBN / 16;  // 16-key tiles per block
   constexpr int QT = kAttnQW / 16;  // 16-query tiles per wave
@@ -169,11 +169,19 @@ __global__ __launch_bounds__(256) void attention_fwd_kernel(AttnParams p) {
     m[qt] = -__builtin_inff();
     l[qt] = 0.f;
   }
+  // scores are scaled by |scale| log2 e > 0 (the host passes 2^-100 for a
+  // zero scale: exp2 of anything that small is exactly 1, as for 0); a
+  // negative scale flips the sign of Q instead (exact)
   const float sl2 = p.scale_log2;
+  if (p.negate_q) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int kk = 0; kk < DK; ++kk) qf[qt][kk] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  }
 
   wait_vm_barrier<0>();
   for (int j = 0; j < nblk; ++j) {
-    const uint32_t stage = lds0 + (j & 1) * S::STAGE;
     if (j + 1 < nblk) cp.issue(wave, kr, vr, (j + 1) * kAttnBN, n, lds0 + ((j + 1) & 1) * S::STAGE);
     const int kb = j * kAttnBN;
     // a causal block entirely after this wave's last query adds nothing
@@ -196,40 +204,72 @@ __global__ __launch_bounds__(256) void attention_fwd_kernel(AttnParams p) {
           for (int qt = 0; qt < QT; ++qt) st[kt][qt] = mfma16x16x32(DT{}, a, qf[qt][kk], st[kt][qt]);
         }
 
-      // online softmax (base 2) and P^T operands
+      // masked keys (past the end; causal: after the query) get a raw score
+      // of -inf; only blocks that hold such keys pay for the test
+      if (kb + kAttnBN > n || (CAUSAL && kb + kAttnBN - 1 > q0w)) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int key = kb + 16 * kt + 4 * fk + r;
+              const bool ok = key < n && (!CAUSAL || key <= q0w + 16 * qt + fr);
+              st[kt][qt][r] = ok ? st[kt][qt][r] : -__builtin_inff();
+            }
+      }
+
+      // block max of the scaled scores per query (sl2 > 0: the max commutes
+      // with the scaling; all keys masked: -inf)
+      float bm[QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        float x = -__builtin_inff();
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x = __builtin_fmaxf(x, st[kt][qt][r]);
+        x = __builtin_fmaxf(x, __shfl_xor(x, 16));
+        bm[qt] = __builtin_fmaxf(x, __shfl_xor(x, 32)) * sl2;
+      }
+
+      // Lazy rescaling: the reference m of a query moves only when the block
+      // max exceeds it by more than kLazy (log2 units), so p = exp2(s - m)
+      // stays <= 2^kLazy; the output and the sum share the same stale m, so
+      // their quotient is unchanged.  The wave rescales only when one of its
+      // queries needs it.
+      constexpr float kLazy = 8.f;
+      bool need = false;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) need |= bm[qt] > m[qt] + kLazy;
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const bool up = bm[qt] > m[qt] + kLazy;
+          const float corr = up ? __builtin_amdgcn_exp2f(m[qt] - bm[qt]) : 1.f;  // m = -inf: corr = 0
+          m[qt] = up ? bm[qt] : m[qt];
+          l[qt] *= corr;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) o[dt][qt] *= corr;
+        }
+      }
+
+      // P^T operands and the partial sums: p = exp2(s sl2 - m); a masked key
+      // (s = -inf) gives 0
       u32x4 pb[QT][KT / 2];
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        const int query = q0w + 16 * qt + fr;
-        float bm = -__builtin_inff();
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = kb + 16 * kt + 4 * fk + r;
-            const bool ok = key < n && (!CAUSAL || key <= query);
-            const float s = ok ? st[kt][qt][r] * sl2 : -__builtin_inff();
-            st[kt][qt][r] = s;
-            bm = __builtin_fmaxf(bm, s);
-          }
-        bm = __builtin_fmaxf(bm, __shfl_xor(bm, 16));
-        bm = __builtin_fmaxf(bm, __shfl_xor(bm, 32));
-        const float mn = __builtin_fmaxf(m[qt], bm);
-        const float mu = mn == -__builtin_inff() ? 0.f : mn;  // nothing visible yet: keep exp2 finite
-        const float corr = __builtin_amdgcn_exp2f(m[qt] - mu);
-        m[qt] = mn;
-        float ps = 0.f;
+        const float mu = m[qt] == -__builtin_inff() ? 0.f : m[qt];  // nothing visible yet
         float pv[KT][4];
+        float ps = 0.f;
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            pv[kt][r] = __builtin_amdgcn_exp2f(st[kt][qt][r] - mu);
+            pv[kt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kt][qt][r], sl2, -mu));
             ps += pv[kt][r];
           }
-        l[qt] = l[qt] * corr + ps;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt][qt] *= corr;
+        l[qt] += ps;
 #pragma unroll
         for (int u = 0; u < KT / 2; ++u)
           pb[qt][u] = u32x4{pack2(DT{}, pv[2 * u][0], pv[2 * u][1]), pack2(DT{}, pv[2 * u][2], pv[2 * u][3]),

@@ -143,15 +143,16 @@ __device__ __forceinline__ float hi_to_f32(F16, uint32_t w) {
 __device__ __forceinline__ float lo_to_f32(BF16, uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float hi_to_f32(BF16, uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
+// Two values converted as one two-element vector: one v_cvt_pk_f16_f32 /
+// v_cvt_pk_bf16_f32 (round to nearest even) instead of two conversions and a
+// shift-or.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack2(F16, float a, float b) {
-  const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)a);
-  const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)b);
-  return lo | (hi << 16);
+  return __builtin_bit_cast(uint32_t, f16x2{(_Float16)a, (_Float16)b});
 }
 __device__ __forceinline__ uint32_t pack2(BF16, float a, float b) {
-  const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)a);
-  const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)b);
-  return lo | (hi << 16);
+  return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
 }
 
 // ---------------------------------------------------------------------------

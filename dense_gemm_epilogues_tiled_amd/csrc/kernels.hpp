@@ -59,7 +59,8 @@ struct AttnParams {
   int N;            // sequence length
   int q_blocks;     // query blocks per (batch, head)
   int groups;       // workgroups: batch * heads * q_blocks
-  float scale_log2; // scale * log2(e)
+  float scale_log2; // |scale| * log2(e)
+  int negate_q;     // scale < 0: the kernel flips the sign of Q
 };
 
 typedef hipError_t (*VectorAddFn)(const VectorAddParams&, hipStream_t);
