@@ -28,7 +28,8 @@
 // (g = l / 16), and V^T as its A operand read with ds_read_b64_tr_b16 using
 // the same key order (an MFMA sums over k in any order, as long as both
 // operands agree).  So P never leaves the registers and is never shuffled;
-// per-query statistics need only the 4 lanes that share a query (xor 16, 32).
+// per-query statistics need only the 4 lanes that share a query (lane-swap
+// instructions across rows of 16 and halves of 32 lanes).
 // The online softmax works in base 2 (exp2 on scale * log2 e * score), keeps
 // per-lane partial sums (the 4 lanes of a query are rescaled by the same
 // factors) and reduces them once at the end.
@@ -57,14 +58,41 @@ struct AttnShape {
   static_assert(KCOPIES * 1024 * kAttnWaves == KBYTES && VCOPIES * 1024 * kAttnWaves == VBYTES, "1 KB pieces");
 };
 
+// V tiles are n-contiguous (a key row of D values) with 32-byte pairs of
+// 16-byte chunks XOR-swizzled per row.  The transposing reads of one wave
+// touch 4 consecutive keys per 16-lane group and the groups start 4 keys
+// apart, so the swizzle takes key bits 0-1 (rows within a group) and bit 2
+// (neighbouring groups): the 32 lanes served together hit 8 distinct pairs.
+__device__ __forceinline__ int v_swz(int key) { return (key & 3) | (((key >> 2) & 1) << 2); }
+template <int D>
+__device__ __forceinline__ int v_off(int key, int chunk) {
+  return key * (D * 2) + 16 * ((((chunk >> 1) ^ v_swz(key)) << 1) | (chunk & 1));
+}
+
+// x combined with the value of the same register in lanes l ^ 16 and l ^ 32
+// (the four lanes that hold one query's scores), via the gfx950 lane-swap
+// instructions (VALU, no LDS round trip).  The words pass by value: a bit
+// cast of a vector element in place would read element 0.
+__device__ __forceinline__ float w2f(uint32_t w) { return __builtin_bit_cast(float, w); }
+__device__ __forceinline__ uint32_t f2w(float f) { return __builtin_bit_cast(uint32_t, f); }
+template <bool MAX>
+__device__ __forceinline__ float reduce_4lanes(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(f2w(x), f2w(x), false, false);  // rows of 16 lanes, pairwise
+  const uint32_t a0 = a[0], a1 = a[1];
+  x = MAX ? __builtin_fmaxf(w2f(a0), w2f(a1)) : w2f(a0) + w2f(a1);
+  const auto b = __builtin_amdgcn_permlane32_swap(f2w(x), f2w(x), false, false);  // halves of 32 lanes
+  const uint32_t b0 = b[0], b1 = b[1];
+  return MAX ? __builtin_fmaxf(w2f(b0), w2f(b1)) : w2f(b0) + w2f(b1);
+}
+
 // Per-lane source offsets (bytes from the block's first key row) of this
 // wave's copies, chosen so that the LDS image of a block is the swizzled
 // layout the fragment reads expect: K rows k-contiguous (kc_off), V rows
-// n-contiguous (nc_off).
+// n-contiguous (v_off).
 template <int D>
 struct AttnCopies {
   int k_off[AttnShape<D>::KCOPIES], k_row[AttnShape<D>::KCOPIES];
-  int v_off[AttnShape<D>::VCOPIES], v_row[AttnShape<D>::VCOPIES];
+  int v_src[AttnShape<D>::VCOPIES], v_row[AttnShape<D>::VCOPIES];
 
   __device__ __forceinline__ void init(int wave, int lane) {
     constexpr int KCH = D / 8;
@@ -82,8 +110,8 @@ struct AttnCopies {
       const int pos = 1024 * (wave + kAttnWaves * j) + 16 * lane;
       const int row = pos / (D * 2);
       const int slot = (pos % (D * 2)) / 16;
-      const int chunk = (((slot >> 1) ^ nc_swz(row)) << 1) | (slot & 1);
-      v_off[j] = row * D * 2 + chunk * 16;
+      const int chunk = (((slot >> 1) ^ v_swz(row)) << 1) | (slot & 1);
+      v_src[j] = row * D * 2 + chunk * 16;
       v_row[j] = row;
     }
   }
@@ -100,7 +128,7 @@ struct AttnCopies {
 #pragma unroll
     for (int j = 0; j < AttnShape<D>::VCOPIES; ++j)
       dma16(vr, stage + AttnShape<D>::KBYTES + 1024 * (wave + kAttnWaves * j),
-            v_row[j] < rows_left ? base + v_off[j] : kOOB);
+            v_row[j] < rows_left ? base + v_src[j] : kOOB);
   }
 };
 
@@ -229,8 +257,7 @@ __global__ __launch_bounds__(256, 2) void attention_fwd_kernel(AttnParams p) {
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) x = __builtin_fmaxf(x, st[kt][qt][r]);
-        x = __builtin_fmaxf(x, __shfl_xor(x, 16));
-        bm[qt] = __builtin_fmaxf(x, __shfl_xor(x, 32)) * sl2;
+        bm[qt] = reduce_4lanes<true>(x) * sl2;
       }
 
       // Lazy rescaling: the reference m of a query moves only when the block
@@ -285,8 +312,8 @@ __global__ __launch_bounds__(256, 2) void attention_fwd_kernel(AttnParams p) {
         for (int dt = 0; dt < NDT; ++dt) {
           const int chunk = 2 * dt + ((fr & 3) >> 1);
           const int key = 32 * u + 4 * fk + (fr >> 2);
-          const u32x2 lo = lds_read_tr8(sV, nc_off<D>(key, chunk) + 8 * (fr & 1));
-          const u32x2 hi = lds_read_tr8(sV, nc_off<D>(key + 16, chunk) + 8 * (fr & 1));
+          const u32x2 lo = lds_read_tr8(sV, v_off<D>(key, chunk) + 8 * (fr & 1));
+          const u32x2 hi = lds_read_tr8(sV, v_off<D>(key + 16, chunk) + 8 * (fr & 1));
           const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
           for (int qt = 0; qt < QT; ++qt) o[dt][qt] = mfma16x16x32(DT{}, a, pb[qt][u], o[dt][qt]);
@@ -300,10 +327,7 @@ __global__ __launch_bounds__(256, 2) void attention_fwd_kernel(AttnParams p) {
   // finish: O = O^T / l, lane writes dims 16 dt + 4 fk .. +3 of its query
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    float lt = l[qt];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
-    const float inv = 1.0f / lt;
+    const float inv = 1.0f / reduce_4lanes<false>(l[qt]);
     const int query = q0w + 16 * qt + fr;
     if (query < n) {
       uint16_t* orow = static_cast<uint16_t*>(p.O) + (head * n + query) * (int64_t)D;
