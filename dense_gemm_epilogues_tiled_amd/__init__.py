@@ -74,6 +74,17 @@ class tg_gemm_args(ctypes.Structure):
     ]
 
 
+class tg_autotune_entry(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("b_col_major", ctypes.c_int32), ("kind", ctypes.c_int32),
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("config", tg_tile_config),
+                ("us", ctypes.c_float), ("candidates", ctypes.c_int32), ("valid", ctypes.c_int32)]
+
+    def as_dict(self) -> dict:
+        d = {n: getattr(self, n) for n, _ in self._fields_ if n != "config"}
+        d["config"] = self.config.as_dict()
+        return d
+
+
 # Every function include/tg.h declares, with its ctypes signature.
 _SIGNATURES = {
     "tg_gemm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
@@ -88,6 +99,16 @@ _SIGNATURES = {
     "tg_attention_fwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
+    "tg_gemm_autotune_workspace_size": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                                       ctypes.POINTER(ctypes.c_int64)]),
+    "tg_gemm_autotune": (ctypes.c_int, [ctypes.POINTER(tg_gemm_args), ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                        ctypes.POINTER(tg_autotune_entry), ctypes.c_void_p]),
+    "tg_autotune_cache_size": (ctypes.c_int, []),
+    "tg_autotune_cache_get": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(tg_autotune_entry)]),
+    "tg_autotune_cache_clear": (ctypes.c_int, []),
+    "tg_autotune_cache_save": (ctypes.c_int, [ctypes.c_char_p]),
+    "tg_autotune_cache_load": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int),
+                                              ctypes.POINTER(ctypes.c_int)]),
     "tg_num_configs": (ctypes.c_int, []),
     "tg_get_config": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(tg_tile_config)]),
     "tg_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -152,6 +173,48 @@ def tg_row_softmax(X: int | None, Y: int | None, rows: int, cols: int, dtype: in
 def tg_attention_fwd(Q: int | None, K: int | None, V: int | None, O: int | None, batch: int, heads: int,
                      seq_len: int, head_dim: int, dtype: int, causal: int, scale: float, stream: int | None) -> int:
     return load().tg_attention_fwd(Q, K, V, O, batch, heads, seq_len, head_dim, dtype, causal, scale, stream)
+
+
+def tg_gemm_autotune_workspace_size(M: int, N: int, epilogue: int):
+    """Returns (status, bytes)."""
+    out = ctypes.c_int64(0)
+    rc = load().tg_gemm_autotune_workspace_size(M, N, epilogue, ctypes.byref(out))
+    return rc, out.value
+
+
+def tg_gemm_autotune(args: tg_gemm_args | None, workspace: int | None, workspace_bytes: int, iters: int,
+                     stream: int | None):
+    """Returns (status, tg_autotune_entry)."""
+    res = tg_autotune_entry()
+    rc = load().tg_gemm_autotune(ctypes.byref(args) if args is not None else None, workspace, workspace_bytes, iters,
+                                 ctypes.byref(res), stream)
+    return rc, res
+
+
+def tg_autotune_cache_size() -> int:
+    return load().tg_autotune_cache_size()
+
+
+def tg_autotune_cache_get(index: int):
+    """Returns (status, tg_autotune_entry)."""
+    out = tg_autotune_entry()
+    rc = load().tg_autotune_cache_get(index, ctypes.byref(out))
+    return rc, out
+
+
+def tg_autotune_cache_clear() -> int:
+    return load().tg_autotune_cache_clear()
+
+
+def tg_autotune_cache_save(path: str | None) -> int:
+    return load().tg_autotune_cache_save(path.encode() if path is not None else None)
+
+
+def tg_autotune_cache_load(path: str | None):
+    """Returns (status, loaded, skipped)."""
+    a, b = ctypes.c_int(0), ctypes.c_int(0)
+    rc = load().tg_autotune_cache_load(path.encode() if path is not None else None, ctypes.byref(a), ctypes.byref(b))
+    return rc, a.value, b.value
 
 
 def tg_num_configs() -> int:
@@ -290,6 +353,46 @@ def attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, causal: bool = 
                           int(bool(causal)), sc, stream if stream is not None else _stream_handle(Q.device))
     if rc != TG_OK:
         raise TgError(rc, "tg_attention_fwd")
+    return out
+
+
+def autotune(A: torch.Tensor, B: torch.Tensor, bias: torch.Tensor | None = None, epilogue: str = "none",
+             b_col_major: bool = False, alpha: float = 1.0, out: torch.Tensor | None = None, iters: int = 10,
+             stream: int | None = None) -> dict:
+    """Tune the configuration for this problem (tg_gemm_autotune) and cache it;
+    `out` (allocated if None) receives the winner's result.  Returns the cache
+    entry as a dict (config, us, candidates, valid) plus "out"."""
+    if epilogue not in EPILOGUES:
+        raise ValueError(f"unknown epilogue {epilogue!r}")
+    epi = EPILOGUES[epilogue]
+    if A.dtype not in DTYPES or B.dtype != A.dtype or not (A.is_cuda and B.is_cuda):
+        raise ValueError("A and B must be fp16 / bf16 GPU tensors of one dtype")
+    M, K = A.shape
+    N = B.shape[0] if b_col_major else B.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32 if epi == TG_EPI_SOFTMAX else A.dtype, device=A.device)
+    rc, need = tg_gemm_autotune_workspace_size(M, N, epi)
+    if rc != TG_OK:
+        raise TgError(rc, "tg_gemm_autotune_workspace_size")
+    ws = torch.empty(need + 256, dtype=torch.uint8, device=A.device)
+    base = (ws.data_ptr() + 255) // 256 * 256
+    args = tg_gemm_args(A.data_ptr(), B.data_ptr(), bias.data_ptr() if bias is not None else None, out.data_ptr(),
+                        M, N, K, DTYPES[A.dtype], epi, int(bool(b_col_major)), float(alpha), -1, 0, -1)
+    rc, res = tg_gemm_autotune(args, base, need, int(iters), stream if stream is not None else _stream_handle(A.device))
+    if rc != TG_OK:
+        raise TgError(rc, "tg_gemm_autotune")
+    d = res.as_dict()
+    d["out"] = out
+    return d
+
+
+def autotune_cache() -> list[dict]:
+    out = []
+    for i in range(tg_autotune_cache_size()):
+        rc, e = tg_autotune_cache_get(i)
+        if rc != TG_OK:
+            raise TgError(rc, "tg_autotune_cache_get")
+        out.append(e.as_dict())
     return out
 
 

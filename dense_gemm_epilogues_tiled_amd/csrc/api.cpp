@@ -91,7 +91,7 @@ int softmax_capacity(const tg_tile_config& v) { return v.bn; }
 int64_t tiles_of(const tg_tile_config& c, int64_t M, int64_t N) { return cdiv(M, c.bm) * cdiv(N, c.bn); }
 
 // Lookup: baked entry for the exact shape, else the fallback rule.
-Choice choose(int64_t M, int64_t N, int64_t K, int dtype, int epilogue, int b_col_major) {
+Choice choose_default(int64_t M, int64_t N, int64_t K, int dtype, int epilogue, int b_col_major) {
   const Registry& R = registry();
   const int kind = epilogue == TG_EPI_SOFTMAX ? 1 : 0;
   for (int i = 0; i < kNumTable; ++i) {
@@ -133,7 +133,41 @@ Choice choose(int64_t M, int64_t N, int64_t K, int dtype, int epilogue, int b_co
   return {best, R.cfg[best].group_m, R.cfg[best].xcd_remap};
 }
 
+// Lookup: a run-time autotuned entry for the exact shape first (autotune.hip),
+// then the baked table and the fallback rule.
+Choice choose(int64_t M, int64_t N, int64_t K, int dtype, int epilogue, int b_col_major) {
+  const int kind = epilogue == TG_EPI_SOFTMAX ? 1 : 0;
+  Choice c;
+  if (autotune_lookup(dtype, b_col_major, kind, M, N, K, &c.variant, &c.group_m, &c.xcd_remap) &&
+      c.variant >= 0 && c.variant < registry().n && registry().cfg[c.variant].kind == kind)
+    return c;
+  return choose_default(M, N, K, dtype, epilogue, b_col_major);
+}
+
 }  // namespace
+
+// Internal interface for the autotuner (kernels.hpp).
+int num_tile_configs() { return registry().n; }
+
+const tg_tile_config* tile_config(int id) {
+  return id >= 0 && id < registry().n ? &registry().cfg[id] : nullptr;
+}
+
+bool tile_config_runs(int id, int dtype, int b_col_major, int64_t N) {
+  const Registry& R = registry();
+  if (id < 0 || id >= R.n || (dtype != TG_DTYPE_F16 && dtype != TG_DTYPE_BF16) || (b_col_major & ~1)) return false;
+  if (R.cfg[id].kind == TG_KERNEL_GEMM) return R.gemm[id].fn[dtype][b_col_major] != nullptr;
+  return R.softmax[id - R.n_gemm].fn[dtype][b_col_major] != nullptr && N <= softmax_capacity(R.cfg[id]);
+}
+
+void default_choice(int64_t M, int64_t N, int64_t K, int dtype, int epilogue, int b_col_major, int* variant,
+                    int* group_m, int* xcd_remap) {
+  const Choice c = choose_default(M, N, K, dtype, epilogue, b_col_major);
+  *variant = c.variant;
+  *group_m = c.group_m;
+  *xcd_remap = c.xcd_remap;
+}
+
 }  // namespace tg
 
 using namespace tg;

@@ -1,0 +1,317 @@
+// autotune.hip -- run-time per-shape tile-configuration search and its cache.
+//
+// The TileLang pages tune a GEMM's schedule per matrix shape: a search space
+// over tile sizes, warp counts and pipelining, keyed on (M, N, K); every
+// candidate is compiled, benchmarked and validated, and the winner is cached
+// so the search is paid for once ("TileLang: Criando Kernels ..."
+// (noticiai.com.br), section "Exploracao de schedules com autotuning"; the
+// edgex.exchange page's autotuning paragraph; spaxe.top, autotuning
+// paragraph).  Here every candidate is already compiled (the variants of
+// gemm.hip / softmax.hip), so a search times each compatible variant -- and,
+// for the 2-D tiled kernels, each raster band height and the per-XCD
+// regrouping -- on the caller's own buffers, checks its output against the
+// output of the default choice on the device, and stores the fastest valid
+// one.  tg_gemm / tg_gemm_ex / tg_gemm_query_config consult this cache before
+// the baked table.  The cache can be written to and read from a text file.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/tg.h"
+#include "kernels.hpp"
+
+namespace tg {
+
+namespace {
+
+std::mutex g_mu;
+std::vector<tg_autotune_entry> g_cache;  // one entry per tuned problem
+
+bool same_key(const tg_autotune_entry& e, int dtype, int b_col_major, int kind, int64_t M, int64_t N, int64_t K) {
+  return e.dtype == dtype && e.b_col_major == b_col_major && e.kind == kind && e.M == M && e.N == N && e.K == K;
+}
+
+void cache_put(const tg_autotune_entry& e) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  for (auto& x : g_cache)
+    if (same_key(x, e.dtype, e.b_col_major, e.kind, e.M, e.N, e.K)) {
+      x = e;
+      return;
+    }
+  g_cache.push_back(e);
+}
+
+// ---------------------------------------------------------------------------
+// Validation on the device: the number of elements of C that differ from the
+// reference output by more than atol + rtol |ref| (or that are not finite
+// where the reference is, or the other way round).  Each block writes its
+// own count; the host adds them.
+// ---------------------------------------------------------------------------
+constexpr int kCmpBlocks = 1024;
+
+__device__ __forceinline__ float out_value(const void* p, int64_t i, int out_kind) {
+  if (out_kind == 2) return static_cast<const float*>(p)[i];
+  const uint32_t w = static_cast<const uint16_t*>(p)[i];
+  if (out_kind == 1) return __builtin_bit_cast(float, w << 16);
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)w);
+}
+
+__global__ __launch_bounds__(256) void count_mismatch_kernel(const void* c, const void* r, int64_t n, int out_kind,
+                                                             float atol, float rtol, unsigned* partial) {
+  unsigned bad = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const float x = out_value(c, i, out_kind), y = out_value(r, i, out_kind);
+    const bool fx = __builtin_isfinite(x), fy = __builtin_isfinite(y);
+    if (fx != fy || (fx && !(__builtin_fabsf(x - y) <= atol + rtol * __builtin_fabsf(y))) ||
+        (!fx && !fy && !(x == y || (x != x && y != y))))
+      ++bad;
+  }
+  __shared__ unsigned red[256];
+  red[threadIdx.x] = bad;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) partial[blockIdx.x] = red[0];
+}
+
+int64_t out_bytes(int64_t M, int64_t N, int epilogue) { return M * N * (epilogue == TG_EPI_SOFTMAX ? 4 : 2); }
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+struct Events {
+  hipEvent_t a = nullptr, b = nullptr;
+  ~Events() {
+    if (a) (void)hipEventDestroy(a);
+    if (b) (void)hipEventDestroy(b);
+  }
+};
+
+}  // namespace
+
+bool autotune_lookup(int dtype, int b_col_major, int kind, int64_t M, int64_t N, int64_t K, int* variant,
+                     int* group_m, int* xcd_remap) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  for (const auto& e : g_cache)
+    if (same_key(e, dtype, b_col_major, kind, M, N, K)) {
+      *variant = e.config.id;
+      *group_m = e.config.group_m;
+      *xcd_remap = e.config.xcd_remap;
+      return true;
+    }
+  return false;
+}
+
+}  // namespace tg
+
+using namespace tg;
+
+extern "C" {
+
+int tg_gemm_autotune_workspace_size(int64_t M, int64_t N, int epilogue, int64_t* bytes) {
+  if (!bytes || M < 0 || N < 0 || epilogue < TG_EPI_NONE || epilogue > TG_EPI_SOFTMAX) return TG_ERR_INVALID_ARG;
+  *bytes = align256(out_bytes(M, N, epilogue)) + kCmpBlocks * (int64_t)sizeof(unsigned);
+  return TG_OK;
+}
+
+int tg_gemm_autotune(const tg_gemm_args* args, void* workspace, int64_t workspace_bytes, int iters,
+                     tg_autotune_entry* result, void* stream) {
+  if (!args || !result || iters < 1 || iters > 1000) return TG_ERR_INVALID_ARG;
+  tg_tile_config probe;
+  int rc = tg_gemm_query_config(args->M, args->N, args->K, args->dtype, args->epilogue, args->b_col_major, &probe);
+  if (rc != TG_OK) return rc;
+  const int kind = args->epilogue == TG_EPI_SOFTMAX ? TG_KERNEL_GEMM_SOFTMAX : TG_KERNEL_GEMM;
+  int64_t need = 0;
+  rc = tg_gemm_autotune_workspace_size(args->M, args->N, args->epilogue, &need);
+  if (rc != TG_OK) return rc;
+  if (args->M == 0 || args->N == 0) return TG_ERR_INVALID_ARG;  // nothing to time
+  if (!workspace || workspace_bytes < need) return TG_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return TG_ERR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  // the reference: the default choice (baked table / rule), written to the workspace
+  int dv, dg, dx;
+  default_choice(args->M, args->N, args->K, args->dtype, args->epilogue, args->b_col_major, &dv, &dg, &dx);
+  tg_gemm_args ref = *args;
+  ref.C = workspace;
+  ref.config_id = dv;
+  ref.group_m = dg > 0 ? dg : 1;
+  ref.xcd_remap = dx;
+  rc = tg_gemm_ex(&ref, stream);
+  if (rc != TG_OK) return rc;
+
+  const int64_t n_out = args->M * args->N;
+  const int out_kind = args->epilogue == TG_EPI_SOFTMAX ? 2 : args->dtype;
+  const float tol = args->epilogue == TG_EPI_SOFTMAX ? 1e-4f : 1e-2f;
+  unsigned* partial = reinterpret_cast<unsigned*>(static_cast<unsigned char*>(workspace) +
+                                                  align256(out_bytes(args->M, args->N, args->epilogue)));
+  const int cmp_blocks = (int)(n_out / 2048 + 1 < kCmpBlocks ? n_out / 2048 + 1 : kCmpBlocks);
+  std::vector<unsigned> host_partial(cmp_blocks);
+
+  Events ev;
+  if (hipEventCreate(&ev.a) != hipSuccess || hipEventCreate(&ev.b) != hipSuccess) return TG_ERR_HIP;
+
+  static const int kGroups[] = {1, 4, 8, 16};
+  tg_gemm_args best = *args;
+  float best_us = -1.f;
+  int tried = 0, valid = 0;
+  for (int id = 0; id < num_tile_configs(); ++id) {
+    const tg_tile_config* cfg = tile_config(id);
+    if (cfg->kind != kind || !tile_config_runs(id, args->dtype, args->b_col_major, args->N)) continue;
+    const int ng = kind == TG_KERNEL_GEMM ? 4 : 1, nx = kind == TG_KERNEL_GEMM ? 2 : 1;
+    for (int gi = 0; gi < ng; ++gi)
+      for (int x = 0; x < nx; ++x) {
+        tg_gemm_args c = *args;
+        c.config_id = id;
+        c.group_m = kind == TG_KERNEL_GEMM ? kGroups[gi] : 1;
+        c.xcd_remap = kind == TG_KERNEL_GEMM ? x : 0;
+        ++tried;
+        if (tg_gemm_ex(&c, stream) != TG_OK) continue;  // e.g. a variant the problem cannot use
+        // validate against the reference
+        hipLaunchKernelGGL(count_mismatch_kernel, dim3(cmp_blocks), dim3(256), 0, s, args->C, workspace, n_out,
+                           out_kind, tol, tol, partial);
+        if (hipGetLastError() != hipSuccess) return TG_ERR_HIP;
+        if (hipMemcpyAsync(host_partial.data(), partial, cmp_blocks * sizeof(unsigned), hipMemcpyDeviceToHost, s) !=
+                hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess)
+          return TG_ERR_HIP;
+        uint64_t bad = 0;
+        for (unsigned v : host_partial) bad += v;
+        if (bad != 0) continue;
+        ++valid;
+        // time: one more warm launch, then `iters` launches between events
+        if (tg_gemm_ex(&c, stream) != TG_OK) continue;
+        if (hipEventRecord(ev.a, s) != hipSuccess) return TG_ERR_HIP;
+        for (int i = 0; i < iters; ++i) (void)tg_gemm_ex(&c, stream);
+        if (hipEventRecord(ev.b, s) != hipSuccess || hipEventSynchronize(ev.b) != hipSuccess) return TG_ERR_HIP;
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, ev.a, ev.b) != hipSuccess) return TG_ERR_HIP;
+        const float us = ms * 1000.f / iters;
+        if (best_us < 0.f || us < best_us) {
+          best_us = us;
+          best = c;
+        }
+      }
+  }
+  if (best_us < 0.f) return TG_ERR_UNSUPPORTED;  // no candidate ran and matched the reference
+
+  tg_autotune_entry e;
+  memset(&e, 0, sizeof(e));
+  e.dtype = args->dtype;
+  e.b_col_major = args->b_col_major;
+  e.kind = kind;
+  e.M = args->M;
+  e.N = args->N;
+  e.K = args->K;
+  e.config = *tile_config(best.config_id);
+  e.config.group_m = best.group_m;
+  e.config.xcd_remap = best.xcd_remap;
+  e.config.b_col_major = args->b_col_major;
+  e.us = best_us;
+  e.candidates = tried;
+  e.valid = valid;
+  cache_put(e);
+  *result = e;
+  // leave the winner's result in C
+  rc = tg_gemm_ex(&best, stream);
+  if (rc != TG_OK) return rc;
+  return hipStreamSynchronize(s) == hipSuccess ? TG_OK : TG_ERR_HIP;
+}
+
+int tg_autotune_cache_size(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  return (int)g_cache.size();
+}
+
+int tg_autotune_cache_get(int index, tg_autotune_entry* out) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!out || index < 0 || index >= (int)g_cache.size()) return TG_ERR_INVALID_ARG;
+  *out = g_cache[index];
+  return TG_OK;
+}
+
+int tg_autotune_cache_clear(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_cache.clear();
+  return TG_OK;
+}
+
+// File format: a first line "tg-autotune-cache 1", then one line per entry:
+//   dtype b_col_major kind M N K id bm bn bk stages waves group_m xcd_remap us
+// The tile fields identify the variant; an entry whose id does not describe
+// the same variant in this library (another build) is skipped on load.
+int tg_autotune_cache_save(const char* path) {
+  if (!path) return TG_ERR_INVALID_ARG;
+  std::vector<tg_autotune_entry> copy;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    copy = g_cache;
+  }
+  FILE* f = fopen(path, "w");
+  if (!f) return TG_ERR_INVALID_ARG;
+  int ok = fprintf(f, "tg-autotune-cache 1\n") > 0;
+  for (const auto& e : copy)
+    ok &= fprintf(f, "%d %d %d %lld %lld %lld %d %d %d %d %d %d %d %d %.3f\n", e.dtype, e.b_col_major, e.kind,
+                  (long long)e.M, (long long)e.N, (long long)e.K, e.config.id, e.config.bm, e.config.bn, e.config.bk,
+                  e.config.stages, e.config.waves, e.config.group_m, e.config.xcd_remap, e.us) > 0;
+  ok &= fclose(f) == 0;
+  return ok ? TG_OK : TG_ERR_INVALID_ARG;
+}
+
+int tg_autotune_cache_load(const char* path, int* loaded, int* skipped) {
+  if (!path) return TG_ERR_INVALID_ARG;
+  FILE* f = fopen(path, "r");
+  if (!f) return TG_ERR_INVALID_ARG;
+  char line[512];
+  int version = 0;
+  if (!fgets(line, sizeof line, f) || sscanf(line, "tg-autotune-cache %d", &version) != 1 || version != 1) {
+    fclose(f);
+    return TG_ERR_INVALID_ARG;
+  }
+  int n_ok = 0, n_skip = 0;
+  while (fgets(line, sizeof line, f)) {
+    int dtype, bcol, kind, id, bm, bn, bk, stages, waves, gm, xcd;
+    long long M, N, K;
+    float us;
+    if (line[0] == '\n' || line[0] == '#') continue;
+    const int got = sscanf(line, "%d %d %d %lld %lld %lld %d %d %d %d %d %d %d %d %f", &dtype, &bcol, &kind, &M, &N,
+                           &K, &id, &bm, &bn, &bk, &stages, &waves, &gm, &xcd, &us);
+    const tg_tile_config* cfg = got == 15 ? tile_config(id) : nullptr;
+    tg_tile_config probe;
+    const bool ok = cfg && cfg->kind == kind && cfg->bm == bm && cfg->bn == bn && cfg->bk == bk &&
+                    cfg->stages == stages && cfg->waves == waves && gm >= 1 && gm <= 4096 && (xcd == 0 || xcd == 1) &&
+                    tile_config_runs(id, dtype, bcol, N) &&
+                    tg_gemm_query_config(M, N, K, dtype, kind == TG_KERNEL_GEMM_SOFTMAX ? TG_EPI_SOFTMAX : TG_EPI_NONE,
+                                         bcol, &probe) == TG_OK;
+    if (!ok) {
+      ++n_skip;
+      continue;
+    }
+    tg_autotune_entry e;
+    memset(&e, 0, sizeof(e));
+    e.dtype = dtype;
+    e.b_col_major = bcol;
+    e.kind = kind;
+    e.M = M;
+    e.N = N;
+    e.K = K;
+    e.config = *cfg;
+    e.config.group_m = gm;
+    e.config.xcd_remap = xcd;
+    e.config.b_col_major = bcol;
+    e.us = us;
+    cache_put(e);
+    ++n_ok;
+  }
+  fclose(f);
+  if (loaded) *loaded = n_ok;
+  if (skipped) *skipped = n_skip;
+  return TG_OK;
+}
+
+}  // extern "C"

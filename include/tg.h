@@ -38,10 +38,12 @@
  *           TG_EPI_SOFTMAX    C_ij = exp(x_ij - max_j x_ij) / sum_j exp(...)
  *                             (bias must be NULL; row length N <= TG_SOFTMAX_MAX_N)
  *  Memory   Every pointer is a device pointer owned by the caller.  The library
- *           never allocates, frees or synchronises; it only enqueues one kernel
- *           on `stream` (a hipStream_t; NULL = the null stream).  It keeps no
- *           mutable state, so concurrent calls from several host threads are
- *           safe.  C must not overlap A, B or bias.
+ *           never allocates or frees device memory; apart from the autotuner
+ *           (tg_gemm_autotune, which times candidates and waits for them) it
+ *           never synchronises and only enqueues one kernel on `stream` (a
+ *           hipStream_t; NULL = the null stream).  Its only mutable state is
+ *           the autotune cache, guarded by a lock, so concurrent calls from
+ *           several host threads are safe.  C must not overlap A, B or bias.
  *  Errors   Every entry point returns a tg_status.  All argument checks run on
  *           the host before any HIP call, so an invalid call touches no device
  *           and enqueues nothing.  A launch failure reported by the runtime
@@ -256,6 +258,81 @@ int tg_row_softmax(const void* X, float* Y, int64_t rows, int64_t cols, int dtyp
  */
 int tg_attention_fwd(const void* Q, const void* K, const void* V, void* O, int64_t batch, int64_t heads,
                      int64_t seq_len, int64_t head_dim, int dtype, int causal, float scale, void* stream);
+
+/*
+ * Run-time autotuning: a per-shape search over the compiled tile
+ * configurations with a cache keyed on the problem, as the pages' autotuner
+ * ("TileLang: Criando Kernels ..." (noticiai.com.br), section "Exploracao de
+ * schedules com autotuning": a search space over tile sizes and warp counts,
+ * keyed on (M, N, K); candidates benchmarked, validated, the winner cached so
+ * the cost is paid once; the edgex.exchange and spaxe.top autotuning
+ * paragraphs).  Every candidate here is already compiled, so a search times
+ * each variant that can run the problem -- for the 2-D tiled kernels with
+ * raster band heights 1, 4, 8, 16 and the per-XCD regrouping off and on --
+ * and keeps the fastest whose output matches the default choice's.
+ *
+ * The cache holds one entry per (dtype, b_col_major, kernel kind, M, N, K).
+ * tg_gemm, tg_gemm_ex (config_id < 0) and tg_gemm_query_config consult it
+ * before the built-in table.  It lives for the process; it can be saved to
+ * and loaded from a text file.
+ */
+typedef struct tg_autotune_entry {
+  int32_t dtype;          /* TG_DTYPE_F16 / TG_DTYPE_BF16 */
+  int32_t b_col_major;
+  int32_t kind;           /* TG_KERNEL_GEMM or TG_KERNEL_GEMM_SOFTMAX */
+  int64_t M, N, K;
+  tg_tile_config config;  /* the chosen variant, with its group_m / xcd_remap */
+  float us;               /* its mean launch time when tuned (as saved, when loaded) */
+  int32_t candidates;     /* candidates tried by the search (0 when loaded) */
+  int32_t valid;          /* of those, ran and matched the reference */
+} tg_autotune_entry;
+
+/* Bytes of device workspace tg_gemm_autotune needs for an M x N output with
+ * this epilogue (a copy of the reference output plus 4 KiB of counters). */
+int tg_gemm_autotune_workspace_size(int64_t M, int64_t N, int epilogue, int64_t* bytes);
+
+/*
+ * tg_gemm_autotune -- search the configurations for the problem `args`
+ * describes (its config_id, group_m and xcd_remap are ignored), store the
+ * winner in the cache and describe it in *result.
+ *
+ * The candidates run on the caller's A, B, bias and C; on return C holds the
+ * winner's result.  workspace: device memory of at least
+ * tg_gemm_autotune_workspace_size bytes, 256-byte aligned, not overlapping
+ * the operands; it receives the default choice's output, against which every
+ * candidate's C is compared on the device element by element (|c - r| <=
+ * 1e-2 + 1e-2 |r| for fp16 / bf16 outputs, 1e-4 + 1e-4 |r| for the fp32
+ * softmax; non-finite values must agree).  Each valid candidate is timed over
+ * `iters` launches (1 .. 1000) between HIP events on `stream`.  The call
+ * blocks until the search is done.
+ * Returns TG_OK; the argument errors of tg_gemm_ex; TG_ERR_INVALID_ARG for
+ * NULL args / result, iters out of range, an empty output (M or N zero) or a
+ * missing / short workspace; TG_ERR_MISALIGNED for a misaligned workspace;
+ * TG_ERR_UNSUPPORTED if no candidate ran and matched; TG_ERR_HIP on a runtime
+ * failure.
+ */
+int tg_gemm_autotune(const tg_gemm_args* args, void* workspace, int64_t workspace_bytes, int iters,
+                     tg_autotune_entry* result, void* stream);
+
+/* Number of cached entries; entry `index` (TG_ERR_INVALID_ARG if out of
+ * range or out is NULL); forget every entry. */
+int tg_autotune_cache_size(void);
+int tg_autotune_cache_get(int index, tg_autotune_entry* out);
+int tg_autotune_cache_clear(void);
+
+/* Write the cache to a text file (first line "tg-autotune-cache 1", then one
+ * line per entry: dtype b_col_major kind M N K id bm bn bk stages waves
+ * group_m xcd_remap us).  TG_ERR_INVALID_ARG if path is NULL or the file
+ * cannot be written. */
+int tg_autotune_cache_save(const char* path);
+
+/* Merge a file written by tg_autotune_cache_save into the cache.  An entry
+ * whose configuration id does not describe the same variant in this library
+ * (another build), or that names a problem the library rejects, is skipped.
+ * *loaded / *skipped (either may be NULL) receive the counts.
+ * TG_ERR_INVALID_ARG if path is NULL, the file cannot be read or its first
+ * line is not the header. */
+int tg_autotune_cache_load(const char* path, int* loaded, int* skipped);
 
 /* Number of compiled tile configurations (ids 0 .. n-1). */
 int tg_num_configs(void);

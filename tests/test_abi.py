@@ -29,7 +29,9 @@ def _declared_functions():
 def test_header_declares_expected_entry_points():
     names = _declared_functions()
     for n in ("tg_gemm", "tg_gemm_ex", "tg_gemm_query_config", "tg_num_configs", "tg_get_config",
-              "tg_status_string", "tg_version", "tg_vector_add", "tg_row_softmax", "tg_attention_fwd"):
+              "tg_status_string", "tg_version", "tg_vector_add", "tg_row_softmax", "tg_attention_fwd",
+              "tg_gemm_autotune", "tg_gemm_autotune_workspace_size", "tg_autotune_cache_size", "tg_autotune_cache_get",
+              "tg_autotune_cache_clear", "tg_autotune_cache_save", "tg_autotune_cache_load"):
         assert n in names
 
 
@@ -43,7 +45,8 @@ def test_library_exports_every_declared_symbol():
 def test_struct_layouts_match_header(tmp_path):
     """The ctypes mirrors have the C compiler's sizes and field offsets."""
     fields = {"tg_tile_config": [f for f, _ in tg.tg_tile_config._fields_],
-              "tg_gemm_args": [f for f, _ in tg.tg_gemm_args._fields_]}
+              "tg_gemm_args": [f for f, _ in tg.tg_gemm_args._fields_],
+              "tg_autotune_entry": [f for f, _ in tg.tg_autotune_entry._fields_]}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "tg.h"', "int main(void) {"]
     for st, fs in fields.items():
         lines.append(f'  printf("{st} %zu\\n", sizeof({st}));')
@@ -56,7 +59,8 @@ def test_struct_layouts_match_header(tmp_path):
     subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
                                                  check=True).stdout.splitlines())
-    for st, cls in (("tg_tile_config", tg.tg_tile_config), ("tg_gemm_args", tg.tg_gemm_args)):
+    for st, cls in (("tg_tile_config", tg.tg_tile_config), ("tg_gemm_args", tg.tg_gemm_args),
+                    ("tg_autotune_entry", tg.tg_autotune_entry)):
         assert int(got[st]) == ctypes.sizeof(cls)
         for f in fields[st]:
             assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, f
