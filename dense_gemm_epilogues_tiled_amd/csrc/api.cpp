@@ -325,7 +325,8 @@ int tg_attention_fwd(const void* Q, const void* K, const void* V, void* O, int64
   const int64_t bm = attention_block_queries();
   const int64_t q_blocks = cdiv(seq_len, bm);
   if (heads > 0 && batch > ((int64_t(1) << 31) - 1) / heads) return TG_ERR_UNSUPPORTED;
-  const int64_t groups = batch * heads * q_blocks;
+  const int64_t units = causal ? (q_blocks + 1) / 2 : q_blocks;  // causal: pairs of query blocks
+  const int64_t groups = batch * heads * units;
   if (groups >= (int64_t(1) << 31)) return TG_ERR_UNSUPPORTED;
   if (groups == 0) return TG_OK;
   if (!Q || !K || !V || !O) return TG_ERR_INVALID_ARG;
@@ -337,6 +338,7 @@ int tg_attention_fwd(const void* Q, const void* K, const void* V, void* O, int64
   p.O = O;
   p.N = (int)seq_len;
   p.q_blocks = (int)q_blocks;
+  p.units = (int)units;
   p.groups = (int)groups;
   // |scale| log2 e, kept strictly positive: a masked score is -inf and
   // -inf * 0 would be NaN; 2^-100 times any finite score is below 2^-25, whose

@@ -155,16 +155,17 @@ __global__ __launch_bounds__(256, 2) void attention_fwd_kernel(AttnParams p) {
 
   // workgroup -> (head, query block): each XCD takes a contiguous range of
   // heads (workgroups are dealt to the 8 XCDs round robin), so a head's K / V
-  // stay in one L2; within a head the query blocks run last-to-first, so the
-  // causal kernel starts its longest blocks first.
+  // stay in one L2; within a head the query blocks run last-to-first.
+  // The causal kernel pairs query block t with block q_blocks - 1 - t (the
+  // longest with the shortest), so every workgroup does the same work.
   const int groups = gridDim.x;
   int lin = blockIdx.x;
   if ((groups & 7) == 0) lin = (lin & 7) * (groups >> 3) + (lin >> 3);
-  const int64_t head = lin / p.q_blocks;
-  const int qb = p.q_blocks - 1 - lin % p.q_blocks;
+  const int64_t head = lin / p.units;
+  const int t = lin % p.units;
+  const int qb_first = p.q_blocks - 1 - t;
+  const int npass = CAUSAL && t != qb_first ? 2 : 1;
   const int n = p.N;
-  const int q0 = qb * kAttnBM;
-  const int q0w = q0 + wave * kAttnQW;
 
   const __amdgpu_buffer_rsrc_t qr = head_rsrc(p.Q, head, n, D);
   const __amdgpu_buffer_rsrc_t kr = head_rsrc(p.K, head, n, D);
@@ -173,6 +174,11 @@ __global__ __launch_bounds__(256, 2) void attention_fwd_kernel(AttnParams p) {
   AttnCopies<D> cp;
   cp.init(wave, lane);
   const uint32_t lds0 = lds_addr(smem);
+
+  for (int pass = 0; pass < npass; ++pass) {
+  const int qb = pass == 0 ? qb_first : t;
+  const int q0 = qb * kAttnBM;
+  const int q0w = q0 + wave * kAttnQW;
   const int kend = CAUSAL ? (q0 + kAttnBM < n ? q0 + kAttnBM : n) : n;
   const int nblk = (kend + kAttnBN - 1) / kAttnBN;
   cp.issue(wave, kr, vr, 0, n, lds0);
@@ -209,6 +215,15 @@ __global__ __launch_bounds__(256, 2) void attention_fwd_kernel(AttnParams p) {
   }
 
   wait_vm_barrier<0>();
+  // The Q loads are complete (the wait above), but the compiler does not see
+  // through that asm and would wait for them again at their first use inside
+  // the loop -- with vmcnt, which also counts the in-flight copies of the
+  // next K / V block, stalling every block until its successor has landed.
+  // Redefining the fragments here makes the compiler's wait happen once.
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk) asm volatile("" : "+v"(qf[qt][kk]));
   for (int j = 0; j < nblk; ++j) {
     if (j + 1 < nblk) cp.issue(wave, kr, vr, (j + 1) * kAttnBN, n, lds0 + ((j + 1) & 1) * S::STAGE);
     const int kb = j * kAttnBN;
@@ -339,6 +354,7 @@ __global__ __launch_bounds__(256, 2) void attention_fwd_kernel(AttnParams p) {
       }
     }
   }
+  }  // pass: the last block's barrier has released the LDS ring for the next pass
 }
 
 template <int D, class DT, bool CAUSAL>

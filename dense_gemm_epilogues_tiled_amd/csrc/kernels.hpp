@@ -58,7 +58,8 @@ struct AttnParams {
   void* O;
   int N;            // sequence length
   int q_blocks;     // query blocks per (batch, head)
-  int groups;       // workgroups: batch * heads * q_blocks
+  int units;        // workgroups per (batch, head): q_blocks, or ceil(q_blocks / 2) causal pairs
+  int groups;       // workgroups: batch * heads * units
   float scale_log2; // |scale| * log2(e)
   int negate_q;     // scale < 0: the kernel flips the sign of Q
 };
