@@ -81,12 +81,19 @@ def measured_traffic(workload: str):
     return d.get("bytes_per_launch")
 
 
-def time_launches(launch, steps: int, warmup: int, stream):
-    """Returns (wall ms per launch, event ms per launch)."""
+def time_launches(launch, steps: int, warmup: int, stream, warm_ms: float = 0.0):
+    """Returns (wall ms per launch, event ms per launch).  At least `warmup`
+    launches, and more until `warm_ms` of wall time has passed (the GPU clocks
+    ramp up under sustained load)."""
     import torch
+    t_end = time.perf_counter() + warm_ms * 1e-3
     with torch.cuda.stream(stream):
         for _ in range(warmup):
             launch()
+        while warm_ms > 0 and time.perf_counter() < t_end:
+            for _ in range(10):
+                launch()
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
@@ -163,7 +170,7 @@ def bandwidth_table(dev, stream, names=None, steps=None, warmup: int = 10) -> di
                 def launch(ad=ad, w=w, out=out):
                     tg.row_softmax(ad, alpha=w.alpha, out=out)
             n = steps or (20 if w.min_bytes() > (1 << 30) else 100)
-            wall, ev = time_launches(launch, n, warmup, stream)
+            wall, ev = time_launches(launch, n, warmup, stream, warm_ms=150.0)
             gbs = w.min_bytes() / (ev * 1e-3) / 1e9
             table[name] = {"kernel": "vector_add_kernel" if w.kind == "vector_add" else "row_softmax_kernel",
                            "workload": w.description, "us": round(ev * 1e3, 3), "us_wall": round(wall * 1e3, 3),
@@ -195,7 +202,7 @@ def attention_table(dev, stream, names=None, steps=None, warmup: int = 5) -> dic
 
             def launch(q=q, k=k, v=v, w=w, out=out):
                 tg.attention(q, k, v, causal=w.causal, scale=w.scale, out=out)
-            wall, ev = time_launches(launch, steps or 20, warmup, stream)
+            wall, ev = time_launches(launch, steps or 20, warmup, stream, warm_ms=150.0)
             tf = w.flops / (ev * 1e-3) / 1e12
             table[name] = {"kernel": "attention_fwd_kernel", "workload": w.description, "us": round(ev * 1e3, 3),
                            "us_wall": round(wall * 1e3, 3), "algorithmic_flops": w.flops, "TFLOP/s": round(tf, 1),

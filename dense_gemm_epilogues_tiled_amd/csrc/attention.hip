@@ -249,7 +249,7 @@ __global__ __launch_bounds__(256, 2) void attention_fwd_kernel(AttnParams p) {
 
       // masked keys (past the end; causal: after the query) get a raw score
       // of -inf; only blocks that hold such keys pay for the test
-      if (kb + kAttnBN > n || (CAUSAL && kb + kAttnBN - 1 > q0w)) {
+      if (__builtin_expect(kb + kAttnBN > n || (CAUSAL && kb + kAttnBN - 1 > q0w), 0)) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
