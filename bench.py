@@ -202,7 +202,8 @@ def attention_table(dev, stream, names=None, steps=None, warmup: int = 5) -> dic
 
             def launch(q=q, k=k, v=v, w=w, out=out):
                 tg.attention(q, k, v, causal=w.causal, scale=w.scale, out=out)
-            wall, ev = time_launches(launch, steps or 20, warmup, stream, warm_ms=150.0)
+            # long-running compute-bound kernel: give the clocks a full second
+            wall, ev = time_launches(launch, steps or 20, warmup, stream, warm_ms=1000.0)
             tf = w.flops / (ev * 1e-3) / 1e12
             table[name] = {"kernel": "attention_fwd_kernel", "workload": w.description, "us": round(ev * 1e3, 3),
                            "us_wall": round(wall * 1e3, 3), "algorithmic_flops": w.flops, "TFLOP/s": round(tf, 1),
