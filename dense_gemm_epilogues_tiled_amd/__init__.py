@@ -332,7 +332,7 @@ def attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, causal: bool = 
     """FlashAttention forward through tg_attention_fwd: O = softmax(scale Q K^T [causal]) V.
 
     Q, K, V: (batch, heads, seq_len, head_dim) contiguous fp16 or bf16 on one GPU
-    (head_dim 128); scale defaults to 1/sqrt(head_dim).  O has Q's shape and dtype.
+    (head_dim 64 or 128); scale defaults to 1/sqrt(head_dim).  O has Q's shape and dtype.
     """
     if Q.dtype not in DTYPES or K.dtype != Q.dtype or V.dtype != Q.dtype:
         raise TypeError("Q, K and V must share one dtype, float16 or bfloat16")

@@ -1,5 +1,5 @@
-// attention.hip -- FlashAttention forward for gfx950 (fp16 / bf16, head dim 128,
-// causal or not):
+// attention.hip -- FlashAttention forward for gfx950 (fp16 / bf16, head dim 64
+// or 128, causal or not):
 //
 //     O = softmax(scale * Q K^T [key j <= query i when causal]) V   per (batch, head)
 //
@@ -48,7 +48,7 @@ constexpr int kAttnBN = 64;                      // keys per block
 
 template <int D>
 struct AttnShape {
-  static_assert(D == 128, "head dim 128 (the n-contiguous V swizzle needs 128 columns)");
+  static_assert(D == 64 || D == 128, "head dim 64 or 128");
   static constexpr int KBYTES = kAttnBN * D * 2;           // one K block in LDS
   static constexpr int VBYTES = kAttnBN * D * 2;           // one V block in LDS
   static constexpr int STAGE = KBYTES + VBYTES;
@@ -61,12 +61,19 @@ struct AttnShape {
 // V tiles are n-contiguous (a key row of D values) with 32-byte pairs of
 // 16-byte chunks XOR-swizzled per row.  The transposing reads of one wave
 // touch 4 consecutive keys per 16-lane group and the groups start 4 keys
-// apart, so the swizzle takes key bits 0-1 (rows within a group) and bit 2
-// (neighbouring groups): the 32 lanes served together hit 8 distinct pairs.
-__device__ __forceinline__ int v_swz(int key) { return (key & 3) | (((key >> 2) & 1) << 2); }
+// apart; the 32 lanes served together (8 rows) must hit distinct banks.
+//   D = 128: a row spans all 64 banks, so the 8 rows need 8 distinct pairs:
+//            the swizzle takes key bits 0-1 and bit 2;
+//   D = 64:  a row spans half of them (odd rows the other half), so rows of
+//            one parity need distinct pairs: key bits 1-2.
+template <int D>
+__device__ __forceinline__ int v_swz(int key) {
+  if constexpr (D == 128) return (key & 3) | (((key >> 2) & 1) << 2);
+  return (key >> 1) & 3;
+}
 template <int D>
 __device__ __forceinline__ int v_off(int key, int chunk) {
-  return key * (D * 2) + 16 * ((((chunk >> 1) ^ v_swz(key)) << 1) | (chunk & 1));
+  return key * (D * 2) + 16 * ((((chunk >> 1) ^ v_swz<D>(key)) << 1) | (chunk & 1));
 }
 
 // x combined with the value of the same register in lanes l ^ 16 and l ^ 32
@@ -110,7 +117,7 @@ struct AttnCopies {
       const int pos = 1024 * (wave + kAttnWaves * j) + 16 * lane;
       const int row = pos / (D * 2);
       const int slot = (pos % (D * 2)) / 16;
-      const int chunk = (((slot >> 1) ^ v_swz(row)) << 1) | (slot & 1);
+      const int chunk = (((slot >> 1) ^ v_swz<D>(row)) << 1) | (slot & 1);
       v_src[j] = row * D * 2 + chunk * 16;
       v_row[j] = row;
     }
@@ -364,11 +371,16 @@ static hipError_t launch_attention(const AttnParams& p, hipStream_t stream) {
                          dim3((unsigned)p.groups), dim3(256), args, 0, stream);
 }
 
+template <int D>
+static AttnFn attention_launcher_d(int dtype, int causal) {
+  if (dtype == TG_DTYPE_F16) return causal ? &launch_attention<D, F16, true> : &launch_attention<D, F16, false>;
+  if (dtype == TG_DTYPE_BF16) return causal ? &launch_attention<D, BF16, true> : &launch_attention<D, BF16, false>;
+  return nullptr;
+}
+
 __host__ AttnFn attention_launcher(int dtype, int head_dim, int causal) {
-  if (head_dim != 128) return nullptr;
-  if (dtype == TG_DTYPE_F16) return causal ? &launch_attention<128, F16, true> : &launch_attention<128, F16, false>;
-  if (dtype == TG_DTYPE_BF16)
-    return causal ? &launch_attention<128, BF16, true> : &launch_attention<128, BF16, false>;
+  if (head_dim == 128) return attention_launcher_d<128>(dtype, causal);
+  if (head_dim == 64) return attention_launcher_d<64>(dtype, causal);
   return nullptr;
 }
 

@@ -246,7 +246,7 @@ int tg_row_softmax(const void* X, float* Y, int64_t rows, int64_t cols, int dtyp
  *  Layout  Q, K, V, O: [batch][heads][seq_len][head_dim] row-major, packed,
  *          device memory owned by the caller, 16-byte aligned.  O must not
  *          overlap Q, K or V.
- *  Limits  head_dim == 128 (else TG_ERR_UNSUPPORTED); 0 <= seq_len <=
+ *  Limits  head_dim 64 or 128 (else TG_ERR_UNSUPPORTED); 0 <= seq_len <=
  *          TG_ATTN_MAX_SEQ; batch, heads >= 0 with batch * heads *
  *          ceil(seq_len / 128) < 2^31 (else TG_ERR_UNSUPPORTED).
  *  scale   finite (usually 1 / sqrt(head_dim)); NaN or infinite:

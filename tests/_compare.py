@@ -45,18 +45,25 @@ def rounding_floor(y: np.ndarray, out_dtype: str) -> float:
     return float(np.linalg.norm((r - y).ravel()) / ny) if ny > 0 else 0.0
 
 
-def assert_accept(g: np.ndarray, y: np.ndarray, out_dtype: str, what: str = "", small: bool = False) -> dict:
+def assert_accept(g: np.ndarray, y: np.ndarray, out_dtype: str, what: str = "", small: bool = False,
+                  floor_factor: float | None = None) -> dict:
     """The acceptance bound.  small=True (edge-case shapes with a few dozen
     outputs) allows the Frobenius error up to 1.5x that of the correctly
     rounded answer when that floor alone exceeds the bound: a bf16 result
     rounded to nearest carries ~1.1e-3 relative RMS error, so on a handful of
-    values the 2e-3 bound is a coin toss even for an exact kernel."""
+    values the 2e-3 bound is a coin toss even for an exact kernel.
+    floor_factor=f applies max(2e-3, f x that floor) at any size: for results
+    whose arithmetic rounds an intermediate to the output type as well (the
+    attention probabilities fed to the matrix units), the error is about
+    sqrt(2) x the rounding floor by construction."""
     s = stats(g, y, out_dtype)
     assert s["finite"], f"{what}: NaN/Inf in GPU output"
     assert s["n_fail"] == 0, f"{what}: {s['n_fail']} of {s['n']} elements outside tolerance, {s}"
     bound = FROB
     if small:
-        bound = max(FROB, 1.5 * rounding_floor(y, out_dtype))
+        floor_factor = 1.5
+    if floor_factor is not None:
+        bound = max(FROB, floor_factor * rounding_floor(y, out_dtype))
     s["frob_bound"] = bound
     assert s["frob_rel"] <= bound, f"{what}: relative Frobenius error {s['frob_rel']:.3e} > {bound:.3e}"
     return s

@@ -271,8 +271,9 @@ def test_stream_wrappers_check_before_launch():
     (dict(causal=2), tg.TG_ERR_INVALID_ARG),
     (dict(scale=float("nan")), tg.TG_ERR_INVALID_ARG),
     (dict(scale=float("inf")), tg.TG_ERR_INVALID_ARG),
-    (dict(head_dim=64), tg.TG_ERR_UNSUPPORTED),
+    (dict(head_dim=32), tg.TG_ERR_UNSUPPORTED),
     (dict(head_dim=96), tg.TG_ERR_UNSUPPORTED),
+    (dict(head_dim=256), tg.TG_ERR_UNSUPPORTED),
     (dict(head_dim=1 << 40), tg.TG_ERR_UNSUPPORTED),
     (dict(seq_len=(1 << 20) + 1), tg.TG_ERR_UNSUPPORTED),
     (dict(batch=1 << 20, heads=1 << 12), tg.TG_ERR_UNSUPPORTED),   # grid of 2^32 workgroups

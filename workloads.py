@@ -206,6 +206,8 @@ ATTN_WORKLOADS = {
                        description="attention fwd, B=4 H=16 N=4096 D=128 fp16 N(0,1), non-causal, scale 1/sqrt(128)"),
     "A2": AttnWorkload("A2", 4, 16, 4096, 128, "f16", True, (711, 712, 713, 714),
                        description="attention fwd, B=4 H=16 N=4096 D=128 fp16 N(0,1), causal, scale 1/sqrt(128)"),
+    "A3": AttnWorkload("A3", 4, 32, 4096, 64, "bf16", False, (721, 722, 723, 724),
+                       description="attention fwd, B=4 H=32 N=4096 D=64 bf16 N(0,1), non-causal, scale 1/sqrt(64)"),
 }
 
 
