@@ -73,15 +73,18 @@ def test_ragged_lengths(dtype, causal, D):
                       floor_factor=FLOOR)
 
 
-@pytest.mark.parametrize("scale", [0.0, 0.02, 0.3])
-def test_scales(scale):
-    print(f"[parity] attention scale={scale}", flush=True)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("scale", [0.0, 0.02, 0.3, -0.125, -1e-3])
+def test_scales(scale, dtype):
+    """Zero (uniform weights), small, large and negative scales (the kernel
+    flips Q's sign bits and uses |scale|)."""
+    print(f"[parity] attention scale={scale} {dtype}", flush=True)
     B, H, N = 1, 2, 300
-    Q, K, V = (workloads.random_matrix((B, H, N, 128), 900 + j, "f16") for j in range(3))
+    Q, K, V = (workloads.random_matrix((B, H, N, 128), 900 + j, dtype) for j in range(3))
     for causal in (False, True):
         O = _run(Q, K, V, causal, scale)
-        y = oracle.attention(Q, K, V, B, H, N, 128, "f16", causal, scale)
-        assert_accept(to_f64(O).reshape(-1), y.reshape(-1), "f16", f"scale={scale} causal={causal}",
+        y = oracle.attention(Q, K, V, B, H, N, 128, dtype, causal, scale)
+        assert_accept(to_f64(O).reshape(-1), y.reshape(-1), dtype, f"scale={scale} causal={causal}",
                       floor_factor=FLOOR)
 
 
