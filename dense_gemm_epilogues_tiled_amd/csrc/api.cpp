@@ -322,7 +322,7 @@ int tg_attention_fwd(const void* Q, const void* K, const void* V, void* O, int64
   if (!isfinite(scale)) return TG_ERR_INVALID_ARG;
   const AttnFn fn = attention_launcher(dtype, (int)(head_dim > 1024 ? 0 : head_dim), causal);
   if (!fn || seq_len > TG_ATTN_MAX_SEQ) return TG_ERR_UNSUPPORTED;
-  const int64_t bm = attention_block_queries();
+  const int64_t bm = attention_block_queries((int)head_dim, causal);
   const int64_t q_blocks = cdiv(seq_len, bm);
   if (heads > 0 && batch > ((int64_t(1) << 31) - 1) / heads) return TG_ERR_UNSUPPORTED;
   const int64_t units = causal ? (q_blocks + 1) / 2 : q_blocks;  // causal: pairs of query blocks

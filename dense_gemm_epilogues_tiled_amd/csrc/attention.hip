@@ -13,8 +13,9 @@
 //
 // gfx950 design
 // -------------
-// A workgroup of 4 waves owns 128 consecutive queries of one (batch, head):
-// 32 per wave, held in registers as MFMA operands for the whole kernel.  Key
+// A workgroup of 4 waves owns 128 consecutive queries of one (batch, head)
+// (256 for the non-causal kernel at head dim 64): 32 (64) per wave, held in
+// registers as MFMA operands for the whole kernel.  Key
 // and value blocks of 64 rows stream through a two-stage LDS ring, copied
 // HBM/L2 -> LDS with the direct 16-byte-per-lane copies (no VGPR staging);
 // keys past the sequence end are zero-filled by the buffer range check.
@@ -42,8 +43,14 @@ namespace tg {
 namespace {
 
 constexpr int kAttnWaves = 4;
-constexpr int kAttnQW = 32;                      // queries per wave
-constexpr int kAttnBM = kAttnWaves * kAttnQW;    // queries per workgroup
+// Queries per wave: 32, or 64 for the non-causal kernel at head dim 64,
+// where the accumulators are half as large -- every wave reads the whole
+// K / V block from LDS, so more queries per wave means fewer LDS bytes per
+// FLOP.  (The causal kernel's masking state does not fit beside 64.)
+template <int D, bool CAUSAL>
+constexpr int attn_qw() { return D == 64 && !CAUSAL ? 64 : 32; }
+template <int D, bool CAUSAL>
+constexpr int attn_bm() { return kAttnWaves * attn_qw<D, CAUSAL>(); }  // queries per workgroup
 constexpr int kAttnBN = 64;                      // keys per block
 
 template <int D>
@@ -151,6 +158,7 @@ template <int D, class DT, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attention_fwd_kernel(AttnParams p) {
   using S = AttnShape<D>;
   constexpr int KT = kAttnBN / 16;  // 16-key tiles per block
+  constexpr int kAttnQW = attn_qw<D, CAUSAL>(), kAttnBM = attn_bm<D, CAUSAL>();
   constexpr int QT = kAttnQW / 16;  // 16-query tiles per wave
   constexpr int DK = D / 32;        // 32-deep slices of the QK^T product
   constexpr int NDT = D / 16;       // 16-row tiles of O^T
@@ -384,6 +392,9 @@ __host__ AttnFn attention_launcher(int dtype, int head_dim, int causal) {
   return nullptr;
 }
 
-__host__ int attention_block_queries() { return kAttnBM; }
+__host__ int attention_block_queries(int head_dim, int causal) {
+  if (head_dim == 64) return causal ? attn_bm<64, true>() : attn_bm<64, false>();
+  return causal ? attn_bm<128, true>() : attn_bm<128, false>();
+}
 
 }  // namespace tg

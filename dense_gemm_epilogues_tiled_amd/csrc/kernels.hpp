@@ -73,7 +73,7 @@ typedef hipError_t (*AttnFn)(const AttnParams&, hipStream_t);
 VectorAddFn vector_add_launcher(int dtype);
 RowSoftmaxFn row_softmax_launcher(int dtype, int64_t cols);
 AttnFn attention_launcher(int dtype, int head_dim, int causal);
-int attention_block_queries();  // queries per attention workgroup
+int attention_block_queries(int head_dim, int causal);  // queries per attention workgroup
 
 typedef hipError_t (*GemmLaunchFn)(const GemmParams&, hipStream_t);
 typedef hipError_t (*SoftmaxLaunchFn)(const SoftmaxParams&, hipStream_t);
