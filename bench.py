@@ -121,14 +121,19 @@ def prepare(w, dev):
     return A, B, bias, A.to(dev), B.to(dev), (bias.to(dev) if bias is not None else None)
 
 
-def cpu_baseline(w, A, B, bias):
+def cpu_baseline(w, A, B, bias, min_seconds: float = 10.0, max_reps: int = 200):
+    """The oracle on the full problem, repeated until `min_seconds` of wall
+    time have passed (a bounded sample of ~10 s of CPU work), mean rate."""
     import oracle
     threads = oracle.default_threads()
     used = oracle.threads_used(threads)
+    reps = 0
     t0 = time.perf_counter()
-    oracle.gemm(A, B, bias, w.M, w.N, w.K, w.dtype, w.epilogue, b_col_major=w.b_col_major, alpha=w.alpha,
-                threads=threads)
-    dt = time.perf_counter() - t0
+    while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_seconds):
+        oracle.gemm(A, B, bias, w.M, w.N, w.K, w.dtype, w.epilogue, b_col_major=w.b_col_major, alpha=w.alpha,
+                    threads=threads)
+        reps += 1
+    dt = (time.perf_counter() - t0) / reps
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -139,8 +144,9 @@ def cpu_baseline(w, A, B, bias):
     except OSError:
         pass
     return {"value": w.flops / dt / 1e12, "unit": "TFLOP/s", "cores": used, "kind": "oracle",
-            "sample": f"the full {w.M}x{w.N}x{w.K} problem once (fp64 triple loop + epilogue, OpenMP over rows)",
-            "seconds": dt, "cpu_model": cpu_model}
+            "sample": f"the full {w.M}x{w.N}x{w.K} problem {reps} times (fp64 triple loop + epilogue, OpenMP over "
+                      f"rows), mean time per problem",
+            "seconds": dt, "repetitions": reps, "cpu_model": cpu_model}
 
 
 def bandwidth_table(dev, stream, names=None, steps=None, warmup: int = 10) -> dict:
