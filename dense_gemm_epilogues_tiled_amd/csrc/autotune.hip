@@ -19,6 +19,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -31,6 +32,7 @@ namespace {
 
 std::mutex g_mu;
 std::vector<tg_autotune_entry> g_cache;  // one entry per tuned problem
+std::atomic<int> g_count{0};             // g_cache.size(): lets a lookup skip the lock while empty
 
 bool same_key(const tg_autotune_entry& e, int dtype, int b_col_major, int kind, int64_t M, int64_t N, int64_t K) {
   return e.dtype == dtype && e.b_col_major == b_col_major && e.kind == kind && e.M == M && e.N == N && e.K == K;
@@ -44,6 +46,7 @@ void cache_put(const tg_autotune_entry& e) {
       return;
     }
   g_cache.push_back(e);
+  g_count.store((int)g_cache.size(), std::memory_order_release);
 }
 
 // ---------------------------------------------------------------------------
@@ -96,6 +99,7 @@ struct Events {
 
 bool autotune_lookup(int dtype, int b_col_major, int kind, int64_t M, int64_t N, int64_t K, int* variant,
                      int* group_m, int* xcd_remap) {
+  if (g_count.load(std::memory_order_acquire) == 0) return false;  // every launch asks; usually nothing tuned
   std::lock_guard<std::mutex> lock(g_mu);
   for (const auto& e : g_cache)
     if (same_key(e, dtype, b_col_major, kind, M, N, K)) {
@@ -238,6 +242,7 @@ int tg_autotune_cache_get(int index, tg_autotune_entry* out) {
 int tg_autotune_cache_clear(void) {
   std::lock_guard<std::mutex> lock(g_mu);
   g_cache.clear();
+  g_count.store(0, std::memory_order_release);
   return TG_OK;
 }
 
