@@ -302,6 +302,10 @@ def main() -> int:
         f"{tflops:.1f} TFLOP/s ({100 * tflops / peak:.1f}% of {peak} TFLOP/s)")
 
     traffic = measured_traffic(w.name)
+    # the shader clock under sustained MFMA load, right after the timed region
+    clk = tg.shader_clock_mhz(dev)
+    log(f"shader clock under MFMA load: {clk['mhz']:.0f} MHz "
+        f"(dense fp16 MFMA peak at that clock {clk['peak_tflops_at_clock']:.1f} TFLOP/s)")
     result = {
         "metric": "TFLOP/s and % of MFMA peak, fp16 GEMM 2048^3 with fused bias+GELU",
         "value": round(tflops, 2),
@@ -321,7 +325,10 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel_us": round(ms_kernel * 1e3, 3), "algorithmic_flops_per_launch": w.flops,
-                     "kernel": "gemm_tile_kernel"},
+                     "kernel": "gemm_tile_kernel",
+                     "clock_mhz_under_mfma_load": round(clk["mhz"], 1),
+                     "peak_at_measured_clock": round(clk["peak_tflops_at_clock"], 1),
+                     "frac_at_measured_clock": round(achieved / clk["peak_tflops_at_clock"], 4)},
     }
 
     if not args.no_table:

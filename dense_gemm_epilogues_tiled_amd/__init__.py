@@ -109,6 +109,7 @@ _SIGNATURES = {
     "tg_autotune_cache_save": (ctypes.c_int, [ctypes.c_char_p]),
     "tg_autotune_cache_load": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int),
                                               ctypes.POINTER(ctypes.c_int)]),
+    "tg_clock_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "tg_num_configs": (ctypes.c_int, []),
     "tg_get_config": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(tg_tile_config)]),
     "tg_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -215,6 +216,10 @@ def tg_autotune_cache_load(path: str | None):
     a, b = ctypes.c_int(0), ctypes.c_int(0)
     rc = load().tg_autotune_cache_load(path.encode() if path is not None else None, ctypes.byref(a), ctypes.byref(b))
     return rc, a.value, b.value
+
+
+def tg_clock_probe(out: int | None, blocks: int, iters: int, stream: int | None) -> int:
+    return load().tg_clock_probe(out, blocks, iters, stream)
 
 
 def tg_num_configs() -> int:
@@ -394,6 +399,28 @@ def autotune_cache() -> list[dict]:
             raise TgError(rc, "tg_autotune_cache_get")
         out.append(e.as_dict())
     return out
+
+
+def shader_clock_mhz(device=None, blocks: int = 1024, iters: int = 300000) -> dict:
+    """The shader clock under sustained MFMA load, from tg_clock_probe: median
+    over workgroups of 100 MHz x shader cycles / constant-counter ticks.  Also
+    returns the constant counter's rate against the host clock (should be
+    ~100 MHz) and the dense fp16 MFMA peak at the measured clock."""
+    import time as _time
+    dev = torch.device(device if device is not None else "cuda:0")
+    out = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
+    torch.cuda.synchronize(dev)
+    t0 = _time.perf_counter()
+    rc = tg_clock_probe(out.data_ptr(), blocks, iters, _stream_handle(dev))
+    if rc != TG_OK:
+        raise TgError(rc, "tg_clock_probe")
+    torch.cuda.synchronize(dev)
+    wall = _time.perf_counter() - t0
+    v = out.view(blocks, 2).cpu().double()
+    mhz = float((100.0 * v[:, 0] / v[:, 1]).median())
+    tick_rate = float(v[:, 1].max()) / wall / 1e6 if wall > 0 else float("nan")  # MHz, lower bound
+    return {"mhz": mhz, "realtime_mhz_vs_host": tick_rate, "blocks": blocks, "iters": iters,
+            "peak_tflops_at_clock": 256 * 4096 * mhz * 1e6 / 1e12}
 
 
 def query_config(M: int, N: int, K: int, dtype: torch.dtype, epilogue: str, b_col_major: bool = False) -> dict:

@@ -21,7 +21,7 @@ ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libtg.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["gemm.hip", "softmax.hip", "stream.hip", "attention.hip", "autotune.hip", "api.cpp"]
+SOURCES = ["gemm.hip", "softmax.hip", "stream.hip", "attention.hip", "autotune.hip", "clock.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",

@@ -334,6 +334,25 @@ int tg_autotune_cache_save(const char* path);
  * line is not the header. */
 int tg_autotune_cache_load(const char* path, int* loaded, int* skipped);
 
+/*
+ * tg_clock_probe -- measurement aid (not part of any computation): the
+ * shader clock under sustained matrix-unit load.  Launches `blocks`
+ * workgroups of 256 threads that each run `iters` iterations of four
+ * independent v_mfma_f32_16x16x32_f16 chains per wave on operands that change
+ * every iteration (random fp16 values in +-[0.5, 1)), and writes for
+ * workgroup b: out[2b] = shader-clock cycles (s_memtime) elapsed around the
+ * loop, out[2b+1] = ticks of the constant 100 MHz counter (s_memrealtime).
+ * clock = 100 MHz x out[2b] / out[2b+1].  The dense MFMA peak at that clock
+ * is 256 CUs x 4096 FLOP/clk x clock; the published 2.5 PFLOP/s assumes
+ * 2.4 GHz.
+ *  out     device memory for 2 * blocks uint64 values, 16-byte aligned, owned
+ *          by the caller.
+ *  Errors  NULL out, blocks outside 1 .. 65536 or iters outside 1 .. 2^24:
+ *          TG_ERR_INVALID_ARG; misaligned out: TG_ERR_MISALIGNED; a rejected
+ *          launch: TG_ERR_HIP.  One kernel is enqueued on `stream`.
+ */
+int tg_clock_probe(unsigned long long* out, int blocks, int iters, void* stream);
+
 /* Number of compiled tile configurations (ids 0 .. n-1). */
 int tg_num_configs(void);
 

@@ -31,7 +31,7 @@ def test_header_declares_expected_entry_points():
     for n in ("tg_gemm", "tg_gemm_ex", "tg_gemm_query_config", "tg_num_configs", "tg_get_config",
               "tg_status_string", "tg_version", "tg_vector_add", "tg_row_softmax", "tg_attention_fwd",
               "tg_gemm_autotune", "tg_gemm_autotune_workspace_size", "tg_autotune_cache_size", "tg_autotune_cache_get",
-              "tg_autotune_cache_clear", "tg_autotune_cache_save", "tg_autotune_cache_load"):
+              "tg_autotune_cache_clear", "tg_autotune_cache_save", "tg_autotune_cache_load", "tg_clock_probe"):
         assert n in names
 
 
@@ -308,3 +308,12 @@ def test_attention_wrapper_checks_before_launch():
         tg.attention(q, q, q)  # CPU tensors are refused
     with pytest.raises(TypeError):
         tg.attention(q.float(), q.float(), q.float())
+
+
+def test_clock_probe_rejects_before_any_hip_call():
+    assert tg.tg_clock_probe(None, 4, 10, None) == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_clock_probe(4096, 0, 10, None) == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_clock_probe(4096, 65537, 10, None) == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_clock_probe(4096, 4, 0, None) == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_clock_probe(4096, 4, (1 << 24) + 1, None) == tg.TG_ERR_INVALID_ARG
+    assert tg.tg_clock_probe(4100, 4, 10, None) == tg.TG_ERR_MISALIGNED
