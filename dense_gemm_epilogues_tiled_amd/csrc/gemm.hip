@@ -49,7 +49,8 @@ struct GemmShape {
   static_assert(B_COL || BN >= 128, "n-contiguous B tiles need 128+ columns");
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile of whole MFMA tiles");
   static_assert(LDS <= 160 * 1024, "LDS of one gfx950 CU");
-  static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
+  static_assert(STAGES >= 2 && STAGES <= 5, "2 to 5 stages");
+  static_assert(BK == 64 || STAGES >= 3, "one-slice steps reuse a slot one step late");
   static_assert((STAGES - 1) * DMA < 64, "vmcnt range");
   static_assert(BM * BN * 2 <= LDS, "the C image fits in the ring");
 };
@@ -101,6 +102,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
 
   // fragment coordinates of this lane
   const int fr = lane & 15, fk = lane >> 4;
+  FragAddr<BN, BK, S::WTM, S::WTN, FN, B_COL> fa;
+  fa.init(wm, wn, fr, fk);
 
   // ---- fragments: one 32-deep slice (kk) of a stage ----
   struct Frags {
@@ -108,12 +111,12 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
     u32x4 b[FN];
   };
   auto load_frags = [&](int slot, int kk, Frags& f) {
-    const unsigned char* sA = smem + slot * S::STAGE;
+    const unsigned char* sA = smem + opaque_sgpr(slot * S::STAGE);
     const unsigned char* sB = sA + S::A_BYTES;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) f.a[i] = read_a_frag<BK>(sA, wm * S::WTM + 16 * i, kk, fr, fk);
+    for (int i = 0; i < FM; ++i) f.a[i] = fa.read_a(sA, i, kk);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) f.b[j] = read_b_frag<BN, BK, B_COL>(sB, wn * S::WTN + 16 * j, kk, fr, fk);
+    for (int j = 0; j < FN; ++j) f.b[j] = fa.read_b(sB, j, kk);
   };
   auto mfma_frags = [&](const Frags& f) {
 #pragma unroll
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
     constexpr int FROM = decltype(from_c)::value, COUNT = decltype(count_c)::value;
     constexpr int NMF = FM * FN;
     constexpr int NRD = FM + FN;  // fragment loads (a B load is 1 or 2 instructions)
-    const unsigned char* sA = smem + rslot * S::STAGE;
+    const unsigned char* sA = smem + opaque_sgpr(rslot * S::STAGE);
     const unsigned char* sB = sA + S::A_BYTES;
     const uint32_t dbase = smem_base + dslot * S::STAGE;
     static_for<NMF>([&](auto t_c) {
@@ -144,9 +147,9 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
         constexpr int ia = r == 0 ? 0 : r - FN;
         if constexpr ((r * NMF) / NRD == t) {
           if constexpr (is_a)
-            fill.a[ia] = read_a_frag<BK>(sA, wm * S::WTM + 16 * ia, kk, fr, fk);
+            fill.a[ia] = fa.read_a(sA, ia, kk);
           else
-            fill.b[r - 1] = read_b_frag<BN, BK, B_COL>(sB, wn * S::WTN + 16 * (r - 1), kk, fr, fk);
+            fill.b[r - 1] = fa.read_b(sB, r - 1, kk);
         }
       });
       // copies c with c * NMF / COUNT == t
@@ -161,19 +164,19 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
     });
   };
 
-  // Publish a stage: wait until at most LATER stages of this wave's copies
-  // (those issued after it) are still in flight, then the workgroup barrier.
-  // Every wave waited for its own LDS reads before the barrier, so passing it
-  // also means no wave reads any earlier stage's slot any more.
-  auto publish_first = [&]() { wait_vm_barrier<(STAGES - 1) * S::DMA>(); };
+  // Publish a stage (two-slice steps): wait until at most STAGES-2 later
+  // steps of this wave's copies are still in flight, then the workgroup
+  // barrier.  Every wave waited for its own LDS reads before the barrier, so
+  // passing it also means no wave reads any earlier stage's slot any more.
   auto publish_next = [&]() { wait_vm_barrier<(STAGES - 2) * S::DMA>(); };
 
   // ---- main loop ----
-  // STAGES steps are in flight before the loop; at every step boundary the
-  // slot just finished is refilled with the step STAGES ahead, so STAGES-1
-  // steps are always in flight while one is computed.  Fragments of the next
-  // 32-deep slice are read from LDS while the MFMAs of the current slice run
-  // (two register buffers F0 / F1 with fixed roles).
+  // Two-slice steps (BK = 64): STAGES steps are in flight before the loop; at
+  // every step boundary the slot just finished is refilled with the step
+  // STAGES ahead, so STAGES-1 steps are always in flight while one is
+  // computed.  Fragments of the next 32-deep slice are read from LDS while
+  // the MFMAs of the current slice run (two register buffers F0 / F1 with
+  // fixed roles).  One-slice steps (BK = 32) are described at their loop.
   constexpr int KK = BK / 32;
   Frags F0, F1;
   // FRONT: every copy of step kt+STAGES is issued in phase B of step kt,
@@ -189,13 +192,13 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
     issue_part(STAGES - 1, STAGES - 1, std::integral_constant<int, 0>{}, std::integral_constant<int, COPIES_B>{});
   } else {
 #pragma unroll
-    for (int s = 0; s < STAGES; ++s) issue_stage(s, s);
+    for (int s = 0; s < STAGES - 1; ++s) issue_stage(s, s);
   }
   if (KT > 0) {
     if constexpr (KK == 2)
       wait_vm_barrier<(STAGES - 2) * S::DMA + COPIES_B>();
     else
-      publish_first();
+      wait_vm_barrier<(STAGES - 2) * S::DMA>();
     load_frags(0, 0, F0);
     if constexpr (KK == 2) {
       // Explicitly interleaved K step (two 32-deep slices):
@@ -222,20 +225,43 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
                 std::integral_constant<int, 0>{});
       mfma_frags(F1);
     } else {
-      int kt = 0;
-      for (; kt + 1 < KT; kt += 2) {
-        publish_next();
-        issue_stage(kt + STAGES, kt % STAGES);
-        load_frags((kt + 1) % STAGES, 0, F1);
-        mfma_frags(F0);
-        if (kt + 2 < KT) {
-          publish_next();
-          issue_stage(kt + 1 + STAGES, (kt + 1) % STAGES);
-          load_frags((kt + 2) % STAGES, 0, F0);
-        }
-        mfma_frags(F1);
+      // One 32-deep slice per K step, one barrier per step.  Step kt runs
+      // its MFMAs (i-major) on the fragments in F and refills F in place
+      // with step kt+1: A fragment i as soon as the MFMAs of row block i are
+      // done, the B fragments in the last FN MFMAs, so one register buffer
+      // serves both steps.  The copies of step kt+STAGES-1 go into the slot
+      // of step kt-1, whose reads (issued during step kt-2) were consumed by
+      // step kt-1's MFMAs: the barrier never waits for LDS reads, only for
+      // the copies of step kt+1, and every copy has STAGES-2 steps to land.
+      using All = std::integral_constant<int, S::DMA>;
+      auto phase = [&](Frags& f, int rslot, int dkt, int dslot, auto count_c) {
+        constexpr int COUNT = decltype(count_c)::value;
+        constexpr int NMF = FM * FN;
+        const unsigned char* sA = smem + opaque_sgpr(rslot * S::STAGE);
+        const unsigned char* sB = sA + S::A_BYTES;
+        const uint32_t dbase = smem_base + dslot * S::STAGE;
+        static_for<NMF>([&](auto t_c) {
+          constexpr int t = decltype(t_c)::value;
+          constexpr int i = t / FN, j = t % FN;
+          acc[i][j] = mfma16x16x32(DT{}, f.b[j], f.a[i], acc[i][j]);
+          if constexpr (i == FM - 1) f.b[j] = fa.read_b(sB, j, 0);
+          if constexpr (j == FN - 1) f.a[i] = fa.read_a(sA, i, 0);
+          if constexpr (COUNT > 0) {
+            static_for<COUNT>([&](auto c_c) {
+              constexpr int c = decltype(c_c)::value;
+              if constexpr ((c * NMF) / COUNT == t)
+                plan.template copy<c>(wave, gA, gB, m0, n0, N, K, dkt * BK, dbase);
+            });
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      };
+      constexpr int IN_FLIGHT = (STAGES - 3) * S::DMA;  // steps kt+2 .. kt+STAGES-2
+      for (int kt = 0; kt + 1 < KT; ++kt) {
+        wait_vm_barrier_only<IN_FLIGHT>();
+        phase(F0, (kt + 1) % STAGES, kt + STAGES - 1, (kt + STAGES - 1) % STAGES, All{});
       }
-      if (kt < KT) mfma_frags(F0);
+      mfma_frags(F0);
     }
   }
   // copies issued past the end of K may still be writing LDS; once every
@@ -285,6 +311,8 @@ __host__ const GemmVariant* gemm_variants(int* count) {
       make_gemm_variant<128, 128, 64, 2, 4, 4>(4),  // 5: two waves per SIMD
       make_gemm_variant<128, 128, 64, 4, 2, 4>(4),  // 6
       make_gemm_variant<128, 128, 64, 2, 4, 4, true>(4),  // 7: as 5, copies issued a whole step earlier
+      make_gemm_variant<256, 256, 32, 2, 4, 5>(8),        // 8: 4 slices of prefetch in the whole 160 KB
+      make_gemm_variant<256, 256, 64, 2, 2, 2>(8),        // 9: one wave per SIMD, 128x128 per wave
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -18,6 +18,25 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// A wave-uniform value the optimiser may not look through.  Used for the
+// byte offset of a ring slot: otherwise loop strength reduction rewrites
+// (k step mod stages) * slot size into one induction variable per LDS read,
+// each a live VGPR, which spills in the kernels with the largest tiles.
+__device__ __forceinline__ int opaque_sgpr(int v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight,
+// then join the workgroup barrier, without waiting for the wave's LDS
+// operations: for a barrier that only publishes direct-to-LDS copies (tracked
+// by vmcnt).
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier_only() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
 // Workgroup id -> output tile.  The hardware deals consecutive workgroup ids
 // to the 8 XCDs in turn; regroup so XCD x owns logical tiles
 // [x*q + min(x, r), ...) (q = G / 8, r = G % 8), then walk the logical order
@@ -108,26 +127,51 @@ struct CopyPlan {
 };
 
 // Fragment reads of one 32-deep slice kk of a stage (A tile at sA, B tile at
-// sB).  A fragment: rows r0 .. r0+15 of the A tile; B fragment: columns
-// c0 .. c0+15 of the B tile.  Each lane ends with the 8 k values of its MFMA
-// operand (see mfma16x16x32).
-template <int BK>
-__device__ __forceinline__ u32x4 read_a_frag(const unsigned char* sA, int r0, int kk, int fr, int fk) {
-  return lds_read16(sA, kc_off<BK>(r0 + fr, 4 * kk + fk));
-}
-template <int BN, int BK, bool B_COL>
-__device__ __forceinline__ u32x4 read_b_frag(const unsigned char* sB, int c0, int kk, int fr, int fk) {
-  if constexpr (B_COL) {
-    return lds_read16(sB, kc_off<BK>(c0 + fr, 4 * kk + fk));
-  } else {
-    // lanes 4q..4q+3 of each 16-lane group read row k = 32kk + 8fk + 4h + q
-    const int chunk = c0 / 8 + ((fr & 3) >> 1);
-    const int k_lo = 32 * kk + 8 * fk + (fr >> 2);
-    const u32x2 lo = lds_read_tr8(sB, nc_off<BN>(k_lo, chunk) + 8 * (fr & 1));
-    const u32x2 hi = lds_read_tr8(sB, nc_off<BN>(k_lo + 4, chunk) + 8 * (fr & 1));
-    return u32x4{lo.x, lo.y, hi.x, hi.y};
+// sB) for the wave at (wm, wn).  A fragment i: rows 16i .. 16i+15 of the
+// wave's A rows; B fragment j: columns 16j .. 16j+15 of its B columns.  Each
+// lane ends with the 8 k values of its MFMA operand (see mfma16x16x32).
+//
+// The per-lane byte offsets are computed once per kernel.  A block of 16 rows
+// leaves the kc_off swizzle unchanged, so A fragment i (and B fragment j of a
+// k-contiguous B) lies a constant 16*i rows past fragment 0.  For a row-major
+// B the swizzle XORs into the column-block bits, so each 16-column block gets
+// its own offset; k + 4 and k + 32 keep nc_swz(k), so the second half of a
+// fragment and the next slice lie constant distances away.  Constant parts
+// become the LDS instructions' immediate offsets: each read costs at most one
+// address add for the stage slot.
+template <int BN, int BK, int WTM, int WTN, int FN, bool B_COL>
+struct FragAddr {
+  static constexpr int KK = BK / 32;
+  int a[KK];
+  int b[B_COL ? KK : FN];
+
+  __device__ __forceinline__ void init(int wm, int wn, int fr, int fk) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) a[kk] = kc_off<BK>(wm * WTM + fr, 4 * kk + fk);
+    if constexpr (B_COL) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) b[kk] = kc_off<BK>(wn * WTN + fr, 4 * kk + fk);
+    } else {
+      // lanes 4q..4q+3 of each 16-lane group read row k = 8fk + 4h + q
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        b[j] = nc_off<BN>(8 * fk + (fr >> 2), (wn * WTN + 16 * j) / 8 + ((fr & 3) >> 1)) + 8 * (fr & 1);
+    }
   }
-}
+  __device__ __forceinline__ u32x4 read_a(const unsigned char* sA, int i, int kk) const {
+    return lds_read16(sA + a[kk], i * 16 * BK * 2);
+  }
+  __device__ __forceinline__ u32x4 read_b(const unsigned char* sB, int j, int kk) const {
+    if constexpr (B_COL) {
+      return lds_read16(sB + b[kk], j * 16 * BK * 2);
+    } else {
+      const unsigned char* q = sB + b[j];
+      const u32x2 lo = lds_read_tr8(q, 32 * kk * BN * 2);
+      const u32x2 hi = lds_read_tr8(q, (32 * kk + 4) * BN * 2);
+      return u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+  }
+};
 
 // bias[n .. n+3] widened to fp32 (zeros without a bias epilogue).
 template <int EPI, class DT>
