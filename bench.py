@@ -343,7 +343,7 @@ def main() -> int:
                     tg.gemm(At, Bt, bt, epilogue=wt.epilogue, b_col_major=wt.b_col_major, alpha=wt.alpha, out=Ct)
 
                 n = 20 if wt.M * wt.N * wt.K > 2 ** 36 else 100
-                wall, ev = time_launches(lt, n, 10, stream)
+                wall, ev = time_launches(lt, n, 10, stream, warm_ms=150.0)
                 tf = wt.flops / (ev * 1e-3) / 1e12
                 gbs = wt.min_bytes() / (ev * 1e-3) / 1e9
                 table[name] = {"us": round(ev * 1e3, 3), "us_wall": round(wall * 1e3, 3), "TFLOP/s": round(tf, 1),

@@ -62,7 +62,8 @@ def pick(values: dict, prefixes) -> tuple[str, float]:
     return name, statistics.median(values[name])
 
 
-def summarize(workload: str, fetch_dir: str, write_dir: str) -> dict:
+def measure(workload: str, fetch_dir: str, write_dir: str) -> dict:
+    """The traffic record of one workload from its two counter passes."""
     sys.path.insert(0, ROOT)
     import bench
     import workloads as W
@@ -89,6 +90,12 @@ def summarize(workload: str, fetch_dir: str, write_dir: str) -> dict:
         "source": "profiles/hbm_traffic_counters.txt",
     }
     rec["bytes_per_launch"] = rec["fetch_bytes"] + rec["write_bytes"]
+    return rec
+
+
+def summarize(workload: str, fetch_dir: str, write_dir: str) -> dict:
+    """measure(), then write profiles/hbm_traffic_<workload>.json and the text summary."""
+    rec = measure(workload, fetch_dir, write_dir)
     with open(os.path.join(PROFILES, f"hbm_traffic_{workload}.json"), "w") as f:
         json.dump(rec, f, indent=1)
     write_text()
