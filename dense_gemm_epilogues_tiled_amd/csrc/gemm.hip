@@ -264,14 +264,15 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
       mfma_frags(F0);
     }
   }
-  // copies issued past the end of K may still be writing LDS; once every
-  // wave is past this barrier the ring is free for the C image
-  wait_vm_barrier<0>();
-
-  // ---- epilogue on the accumulators, written to C through LDS ----
+  // ---- epilogue: finish the accumulators in registers, then write C once
+  // through an LDS image of the tile.  Copies issued past the end of K may
+  // still be writing LDS; once every wave is past the barrier the ring is
+  // free for the image.
   with_epilogue(p.epilogue, [&](auto epi_c) {
-    store_tile_staged<decltype(epi_c)::value, DT, BM, BN, S::NT, FM, FN>(p, acc, smem, m0, n0, wm * S::WTM,
-                                                                          wn * S::WTN, fr, fk, tid);
+    u32x2 out[FM][FN];
+    finish_tile<decltype(epi_c)::value, DT>(p, acc, out, n0, wn * S::WTN, fk);
+    wait_vm_barrier<0>();
+    store_tile_staged<DT, BM, BN, S::NT, FM, FN>(p, out, smem, m0, n0, wm * S::WTM, wn * S::WTN, fr, fk, tid);
   });
 }
 

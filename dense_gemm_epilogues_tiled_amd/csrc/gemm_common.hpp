@@ -215,8 +215,28 @@ __device__ __forceinline__ int c_image_off(int r, int u) {
   return r * (BN * 2) + 8 * (u ^ ((r & 15) << 1));
 }
 
-template <int EPI, class DT, int BM, int BN, int NT, int FM, int FN>
-__device__ __forceinline__ void store_tile_staged(const GemmParams& p, const f32x4 (&acc)[FM][FN],
+// Bias, activation and the one rounding of a wave's accumulator tiles, in
+// registers: out[i][j] holds the 4 results of acc[i][j] packed to 16 bits.
+// It touches no LDS, so it can run before the barrier that frees the operand
+// ring, overlapping other waves' last MFMAs.
+template <int EPI, class DT, int FM, int FN>
+__device__ __forceinline__ void finish_tile(const GemmParams& p, const f32x4 (&acc)[FM][FN], u32x2 (&out)[FM][FN],
+                                            int n0, int c0, int fk) {
+  const int N = p.N;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int n = n0 + c0 + 16 * j + 4 * fk;
+    const f32x4 b = n < N ? load_bias4<EPI, DT>(p, n) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < FM; ++i) out[i][j] = finish4<EPI, DT>(p.alpha, acc[i][j], b);
+  }
+}
+
+// Write finished tiles to C through an LDS image of the BM x BN tile, so each
+// lane stores whole 16-byte row pieces.  The ring must be free (barrier
+// passed) when this starts.
+template <class DT, int BM, int BN, int NT, int FM, int FN>
+__device__ __forceinline__ void store_tile_staged(const GemmParams& p, const u32x2 (&out)[FM][FN],
                                                   unsigned char* smem, int m0, int n0, int r0, int c0, int fr,
                                                   int fk, int tid) {
   static_assert(BM * BN / 8 % NT == 0, "whole rounds of 16-byte pieces");
@@ -224,12 +244,10 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams& p, const f32
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int c = c0 + 16 * j + 4 * fk;  // column inside the tile
-    const int n = n0 + c;
-    const f32x4 b = n < N ? load_bias4<EPI, DT>(p, n) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r = r0 + 16 * i + fr;
-      *reinterpret_cast<u32x2*>(smem + c_image_off<BN>(r, c / 4)) = finish4<EPI, DT>(p.alpha, acc[i][j], b);
+      *reinterpret_cast<u32x2*>(smem + c_image_off<BN>(r, c / 4)) = out[i][j];
     }
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
