@@ -9,9 +9,11 @@ MFMA main loop, register epilogue, single write of C).
 
 Timing: W eager warmup launches (default 2000, ~50 ms: the GPU clocks ramp up
 under load, so a short warmup under-reports the steady state), then K launches
-captured in one HIP graph
-(replayed once untimed to upload it), then the timed region: one replay of
-the K-launch graph between torch.cuda.synchronize() calls.  HIP events
+(default 2000, ~45 ms) captured in one HIP graph (replayed once untimed to
+upload it), then the timed region: one replay of the K-launch graph between
+torch.cuda.synchronize() calls.  In graphs of a few hundred launches each
+dispatch of this kernel was measured ~2.5 us longer than in graphs of 1000+
+launches or in CPU-paced eager launches, so K defaults to a long graph.  HIP events
 recorded on the launch stream around the same replay give the kernel's
 average duration for the roofline.  Inputs stay resident in HBM, so
 repeated launches see warm L2/MALL, as in the pages' warmup-then-average
@@ -113,6 +115,15 @@ def time_launches(launch, steps: int, warmup: int, stream, warm_ms: float = 0.0)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
+
+
+def kernel_name(cfg: dict) -> str:
+    """The kernel a tile configuration launches."""
+    import dense_gemm_epilogues_tiled_amd as tg
+    if cfg["kind"] == tg.TG_KERNEL_GEMM_SOFTMAX:
+        # the LDS-staged variants are built for column-major B only
+        return "gemm_softmax_lds_kernel" if cfg["b_col_major"] == 1 else "gemm_softmax_kernel"
+    return "gemm_ksplit_kernel" if cfg["waves"] == 2 * cfg["wave_m"] * cfg["wave_n"] else "gemm_tile_kernel"
 
 
 def prepare(w, dev):
@@ -226,7 +237,7 @@ def attention_table(dev, stream, names=None, steps=None, warmup: int = 5) -> dic
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=2000,
                     help="untimed launches before the timed region (about 50 ms at the headline shape, "
                          "enough for the GPU clocks to settle)")
@@ -325,7 +336,7 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel_us": round(ms_kernel * 1e3, 3), "algorithmic_flops_per_launch": w.flops,
-                     "kernel": "gemm_tile_kernel",
+                     "kernel": kernel_name(cfg),
                      "clock_mhz_under_mfma_load": round(clk["mhz"], 1),
                      "peak_at_measured_clock": round(clk["peak_tflops_at_clock"], 1),
                      "frac_at_measured_clock": round(achieved / clk["peak_tflops_at_clock"], 4)},
@@ -342,7 +353,7 @@ def main() -> int:
                 def lt(wt=wt, At=At, Bt=Bt, bt=bt, Ct=Ct):
                     tg.gemm(At, Bt, bt, epilogue=wt.epilogue, b_col_major=wt.b_col_major, alpha=wt.alpha, out=Ct)
 
-                n = 20 if wt.M * wt.N * wt.K > 2 ** 36 else 100
+                n = 50 if wt.M * wt.N * wt.K > 2 ** 36 else 1000
                 wall, ev = time_launches(lt, n, 10, stream, warm_ms=150.0)
                 tf = wt.flops / (ev * 1e-3) / 1e12
                 gbs = wt.min_bytes() / (ev * 1e-3) / 1e9

@@ -277,6 +277,181 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
 }
 
 // ---------------------------------------------------------------------------
+// K-split workgroup: 2 groups of WM x WN waves.  Wave s of group 0 and wave s
+// of group 1 own the same (BM/WM) x (BN/WN) output block; in every 64-deep K
+// step group g multiplies the 32-deep slice g, so a wave reads half a step's
+// fragments from LDS: a third less LDS read traffic than 2*WM*WN waves tiling
+// the output, for the same MFMA work per wave.  The loop is the one-slice
+// loop of gemm_tile_kernel (in-place fragment refill, copies into the slot of
+// step kt-1, barriers that wait only for copies).  At the end the two partial
+// accumulators are summed through LDS, each group finishing half of the row
+// blocks of its output block.
+// ---------------------------------------------------------------------------
+// MFMA order of one step over FM x FN tiles: 0 = j-major; 1 = 2x2 blocks of
+// (i, j), block rows first.  Returns i (WHICH = 0) or j (WHICH = 1) of step t.
+template <int ORDER, int FM, int FN>
+constexpr int mfma_coord(int t, int which) {
+  if (ORDER == 0) return which == 0 ? t % FM : t / FM;
+  const int b = t / 4, w = t % 4, ib = b / (FN / 2), jb = b % (FN / 2);
+  return which == 0 ? 2 * ib + w % 2 : 2 * jb + w / 2;
+}
+// Last step of the order that uses row block i (WHICH = 0) or column block j.
+template <int ORDER, int FM, int FN>
+constexpr int last_use(int x, int which) {
+  int last = -1;
+  for (int t = 0; t < FM * FN; ++t)
+    if (mfma_coord<ORDER, FM, FN>(t, which) == x) last = t;
+  return last;
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, int ORDER, bool B_COL, class DT>
+__global__ __launch_bounds__(2 * WM * WN * 64, 1) void gemm_ksplit_kernel(GemmParams p) {
+  constexpr int BK = 64;
+  constexpr int NS = WM * WN, NW = 2 * NS, NT = NW * 64;
+  constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 16, FN = WTN / 16, H = FM / 2;
+  constexpr int A_BYTES = BM * BK * 2, STAGE = (BM + BN) * BK * 2, LDS = STAGES * STAGE;
+  using Plan = CopyPlan<BM, BN, BK, NW, B_COL>;
+  constexpr int DMA = Plan::DMA;
+  constexpr int XBYTES = NS * 2 * H * FN * 1024;  // partial accumulators handed between the groups
+  static_assert(STAGES >= 3 && LDS <= 160 * 1024 && (STAGES - 1) * DMA < 64, "ring");
+  static_assert(FM % 2 == 0 && WTM % 16 == 0 && WTN % 16 == 0, "whole MFMA tiles, even row blocks");
+  static_assert(XBYTES + BM * BN * 2 <= LDS, "partials and the C image fit in the ring");
+
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = wave / NS, sw = wave % NS;
+  const int wm = sw / WN, wn = sw % WN;
+
+  int tile_m, tile_n;
+  map_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, p.xcd_remap, tile_m, tile_n);
+  const int m0 = tile_m * BM, n0 = tile_n * BN;
+  const int M = p.M, N = p.N, K = p.K;
+  const int KT = (K + BK - 1) / BK;
+  const uint16_t* __restrict__ gA = static_cast<const uint16_t*>(p.A);
+  const uint16_t* __restrict__ gB = static_cast<const uint16_t*>(p.B);
+
+  Plan plan;
+  plan.init(wave, lane, m0, n0, M, N, K);
+  const uint32_t smem_base = lds_addr(smem);
+  const int fr = lane & 15, fk = lane >> 4;
+  FragAddr<BN, BK, WTM, WTN, FN, B_COL> fa;
+  fa.init(wm, wn, fr, fk);
+  // this wave's slice: offsets of slice g (a select, not an indexed register array)
+  const int a_lane = g ? fa.a[1] : fa.a[0];
+  auto read_a = [&](const unsigned char* sA, int i) { return lds_read16(sA + a_lane, i * 16 * BK * 2); };
+  auto read_b = [&](const unsigned char* sB, int j) -> u32x4 {
+    if constexpr (B_COL) {
+      return lds_read16(sB + (g ? fa.b[1] : fa.b[0]), j * 16 * BK * 2);
+    } else {
+      const unsigned char* q = sB + fa.b[j] + g * (32 * BN * 2);
+      const u32x2 lo = lds_read_tr8(q, 0);
+      const u32x2 hi = lds_read_tr8(q, 4 * BN * 2);
+      return u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+  };
+
+  auto issue_stage = [&](int kt, int slot) {
+    const uint32_t sbase = smem_base + slot * STAGE;
+    static_for<DMA>([&](auto c_c) {
+      plan.template copy<decltype(c_c)::value>(wave, gA, gB, m0, n0, N, K, kt * BK, sbase);
+    });
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  struct Frags {
+    u32x4 a[FM];
+    u32x4 b[FN];
+  } F;
+  // MFMAs on F (j-major), refilling F in place with the slice of step kt+1
+  // from slot rslot, and the copies of step dkt into slot dslot.
+  auto phase = [&](int rslot, int dkt, int dslot, auto count_c) {
+    constexpr int COUNT = decltype(count_c)::value;
+    constexpr int NMF = FM * FN;
+    const unsigned char* sA = smem + opaque_sgpr(rslot * STAGE);
+    const unsigned char* sB = sA + A_BYTES;
+    const uint32_t dbase = smem_base + dslot * STAGE;
+    static_for<NMF>([&](auto t_c) {
+      constexpr int t = decltype(t_c)::value;
+      constexpr int i = mfma_coord<ORDER, FM, FN>(t, 0), j = mfma_coord<ORDER, FM, FN>(t, 1);
+      acc[i][j] = mfma16x16x32(DT{}, F.b[j], F.a[i], acc[i][j]);
+      // a fragment is refilled right after its last MFMA of the step: in the
+      // j-major order the B fragments (two transposing reads each) go early,
+      // one per column block, and the A fragments in the last FM MFMAs
+      if constexpr (t == last_use<ORDER, FM, FN>(j, 1)) F.b[j] = read_b(sB, j);
+      if constexpr (t == last_use<ORDER, FM, FN>(i, 0)) F.a[i] = read_a(sA, i);
+      if constexpr (COUNT > 0) {
+        static_for<COUNT>([&](auto c_c) {
+          constexpr int c = decltype(c_c)::value;
+          if constexpr ((c * NMF) / COUNT == t) plan.template copy<c>(wave, gA, gB, m0, n0, N, K, dkt * BK, dbase);
+        });
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st) issue_stage(st, st);
+  if (KT > 0) {
+    wait_vm_barrier<(STAGES - 2) * DMA>();
+    {
+      const unsigned char* sA = smem;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) F.a[i] = read_a(sA, i);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) F.b[j] = read_b(sA + A_BYTES, j);
+    }
+    for (int kt = 0; kt + 1 < KT; ++kt) {
+      wait_vm_barrier_only<(STAGES - 3) * DMA>();
+      phase((kt + 1) % STAGES, kt + STAGES - 1, (kt + STAGES - 1) % STAGES, std::integral_constant<int, DMA>{});
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32(DT{}, F.b[j], F.a[i], acc[i][j]);
+  }
+  // every copy landed and every wave is done with the ring
+  wait_vm_barrier<0>();
+
+  // ---- sum the two groups' partials, then the epilogue: group g finishes
+  // row blocks [H g, H g + H) of its output block ----
+  f32x4* xbuf = reinterpret_cast<f32x4*>(smem);
+  auto xidx = [&](int part, int i, int j) { return ((sw * 2 + part) * H * FN + i * FN + j) * 64 + lane; };
+  with_epilogue(p.epilogue, [&](auto epi_c) {
+    constexpr int EPI = decltype(epi_c)::value;
+    auto finish = [&](auto g_c) {
+      constexpr int G = decltype(g_c)::value;
+#pragma unroll
+      for (int i = 0; i < H; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) xbuf[xidx(1 - G, i, j)] = acc[H * (1 - G) + i][j];
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      u32x2 out[H][FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = n0 + wn * WTN + 16 * j + 4 * fk;
+        const f32x4 b = n < N ? load_bias4<EPI, DT>(p, n) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < H; ++i) out[i][j] = finish4<EPI, DT>(p.alpha, acc[H * G + i][j] + xbuf[xidx(G, i, j)], b);
+      }
+      store_tile_staged<DT, BM, BN, NT, H, FN>(p, out, smem + XBYTES, m0, n0, wm * WTM + 16 * H * G, wn * WTN, fr,
+                                               fk, tid);
+    };
+    if (g == 0)
+      finish(std::integral_constant<int, 0>{});
+    else
+      finish(std::integral_constant<int, 1>{});
+  });
+}
+
+// ---------------------------------------------------------------------------
 // Compiled variants.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BK, int WM, int WN, int ST, bool FRONT, bool B_COL, class DT>
@@ -285,6 +460,27 @@ static hipError_t launch_gemm(const GemmParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(WM * WN * 64);
   return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_tile_kernel<BM, BN, BK, WM, WN, ST, FRONT, B_COL, DT>), grid,
                          block, args, 0, stream);
+}
+
+template <int BM, int BN, int WM, int WN, int ST, int OR, bool B_COL, class DT>
+static hipError_t launch_ksplit(const GemmParams& p, hipStream_t stream) {
+  void* args[] = {const_cast<GemmParams*>(&p)};
+  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(2 * WM * WN * 64);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_ksplit_kernel<BM, BN, WM, WN, ST, OR, B_COL, DT>), grid,
+                         block, args, 0, stream);
+}
+
+// waves = 2 * wave_m * wave_n: two groups splitting each K step
+template <int BM, int BN, int WM, int WN, int ST, int OR = 0>
+static GemmVariant make_ksplit_variant(int group_m) {
+  GemmVariant v;
+  v.cfg = tg_tile_config{0, TG_KERNEL_GEMM, BM, BN, 64, ST, 2 * WM * WN, 16, 16, 32, WM, WN, group_m, 1,
+                         ST * (BM + BN) * 64 * 2, -1};
+  v.fn[0][0] = &launch_ksplit<BM, BN, WM, WN, ST, OR, false, F16>;
+  v.fn[0][1] = &launch_ksplit<BM, BN, WM, WN, ST, OR, true, F16>;
+  v.fn[1][0] = &launch_ksplit<BM, BN, WM, WN, ST, OR, false, BF16>;
+  v.fn[1][1] = &launch_ksplit<BM, BN, WM, WN, ST, OR, true, BF16>;
+  return v;
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int ST, bool FRONT = ST == 2>
@@ -314,6 +510,8 @@ __host__ const GemmVariant* gemm_variants(int* count) {
       make_gemm_variant<128, 128, 64, 2, 4, 4, true>(4),  // 7: as 5, copies issued a whole step earlier
       make_gemm_variant<256, 256, 32, 2, 4, 5>(8),        // 8: 4 slices of prefetch in the whole 160 KB
       make_gemm_variant<256, 256, 64, 2, 2, 2>(8),        // 9: one wave per SIMD, 128x128 per wave
+      make_ksplit_variant<128, 128, 2, 2, 4>(8),          // 10: two groups of 4 waves split each K step
+      make_ksplit_variant<128, 128, 2, 2, 4, 1>(8),       // 11: as 10, MFMAs in 2x2 blocks
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -31,7 +31,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_MIB = 256
-KERNEL_PREFIX = {"gemm": ("gemm_tile_kernel", "gemm_softmax"), "stream": ("vector_add", "row_softmax"),
+KERNEL_PREFIX = {"gemm": ("gemm_tile_kernel", "gemm_ksplit_kernel", "gemm_softmax"), "stream": ("vector_add", "row_softmax"),
                  "attention": ("attention_fwd",)}
 
 

@@ -107,7 +107,8 @@ typedef enum tg_kernel_kind {
 /*
  * One compiled tile configuration (read-only; describes a kernel variant).
  * bm x bn output tile per workgroup, bk-deep K steps, `stages` LDS buffers,
- * waves = wave_m * wave_n 64-lane wavefronts per workgroup, MFMA shape
+ * waves 64-lane wavefronts per workgroup: wave_m x wave_n of them tile the
+ * output, or twice that when two wave groups split every K step, MFMA shape
  * mfma_m x mfma_n x mfma_k, group_m = tile rows per L2 raster band,
  * xcd_remap = 1 when workgroups are regrouped so each XCD owns a contiguous
  * block of tiles, lds_bytes = LDS per workgroup, b_col_major = the B layout
