@@ -366,6 +366,17 @@ __global__ __launch_bounds__(2 * WM * WN * 64, 1) void gemm_ksplit_kernel(GemmPa
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // bias of this lane's output columns, fetched now so its latency hides
+  // under the main loop (a bias is passed exactly when the epilogue uses one)
+  u32x2 bias_raw[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int n = n0 + wn * WTN + 16 * j + 4 * fk;
+    bias_raw[j] = (p.bias != nullptr && n < N)
+                      ? *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.bias) + n)
+                      : u32x2{0u, 0u};
+  }
+
   struct Frags {
     u32x4 a[FM];
     u32x4 b[FN];
@@ -421,9 +432,14 @@ __global__ __launch_bounds__(2 * WM * WN * 64, 1) void gemm_ksplit_kernel(GemmPa
   wait_vm_barrier<0>();
 
   // ---- sum the two groups' partials, then the epilogue: group g finishes
-  // row blocks [H g, H g + H) of its output block ----
+  // row blocks [H g, H g + H) of its output block.  The tile goes out in H
+  // rounds, one row block per wave each: finish it, put it in the C image,
+  // barrier, store those rows; the stores of one round drain while the next
+  // round's activations run. ----
   f32x4* xbuf = reinterpret_cast<f32x4*>(smem);
   auto xidx = [&](int part, int i, int j) { return ((sw * 2 + part) * H * FN + i * FN + j) * 64 + lane; };
+  unsigned char* cimg = smem + XBYTES;
+  uint16_t* __restrict__ gC = static_cast<uint16_t*>(p.C);
   with_epilogue(p.epilogue, [&](auto epi_c) {
     constexpr int EPI = decltype(epi_c)::value;
     auto finish = [&](auto g_c) {
@@ -433,16 +449,34 @@ __global__ __launch_bounds__(2 * WM * WN * 64, 1) void gemm_ksplit_kernel(GemmPa
 #pragma unroll
         for (int j = 0; j < FN; ++j) xbuf[xidx(1 - G, i, j)] = acc[H * (1 - G) + i][j];
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      u32x2 out[H][FN];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int n = n0 + wn * WTN + 16 * j + 4 * fk;
-        const f32x4 b = n < N ? load_bias4<EPI, DT>(p, n) : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < H; ++i)
 #pragma unroll
-        for (int i = 0; i < H; ++i) out[i][j] = finish4<EPI, DT>(p.alpha, acc[H * G + i][j] + xbuf[xidx(G, i, j)], b);
-      }
-      store_tile_staged<DT, BM, BN, NT, H, FN>(p, out, smem + XBYTES, m0, n0, wm * WTM + 16 * H * G, wn * WTN, fr,
-                                               fk, tid);
+        for (int j = 0; j < FN; ++j) acc[H * G + i][j] += xbuf[xidx(G, i, j)];
+      static_for<H>([&](auto ih_c) {
+        constexpr int IH = decltype(ih_c)::value;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const u32x2 bb = bias_raw[j];
+          const f32x4 b{lo_to_f32(DT{}, bb.x), hi_to_f32(DT{}, bb.x), lo_to_f32(DT{}, bb.y), hi_to_f32(DT{}, bb.y)};
+          const int r = wm * WTM + 16 * (H * G + IH) + fr;
+          const int c = wn * WTN + 16 * j + 4 * fk;
+          *reinterpret_cast<u32x2*>(cimg + c_image_off<BN>(r, c / 4)) =
+              finish4<EPI, DT>(p.alpha, acc[H * G + IH][j], b);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // rows of round IH: row block (r / 16) % H == IH of every wave's block
+        constexpr int PIECES_PER_ROW = BN / 8, ROWS = BM / H;
+        static_assert(ROWS * PIECES_PER_ROW % NT == 0, "whole rounds of 16-byte pieces");
+#pragma unroll
+        for (int q = tid; q < ROWS * PIECES_PER_ROW; q += NT) {
+          const int rr = q / PIECES_PER_ROW, v = q % PIECES_PER_ROW;
+          const int r = (rr / 16) * (16 * H) + 16 * IH + rr % 16;
+          const int m = m0 + r, n = n0 + 8 * v;
+          const u32x4 val = *reinterpret_cast<const u32x4*>(cimg + c_image_off<BN>(r, 2 * v));
+          if (m < M && n < N) *reinterpret_cast<u32x4*>(gC + (size_t)m * N + n) = val;
+        }
+      });
     };
     if (g == 0)
       finish(std::integral_constant<int, 0>{});
