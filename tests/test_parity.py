@@ -120,6 +120,20 @@ def test_k_zero_gives_epilogue_of_bias(dtype):
     np.testing.assert_allclose(to_f64(C), np.full((M, N), 1.0 / N), rtol=1e-6)
 
 
+@pytest.mark.parametrize("cfg", GEMM_IDS)
+def test_k_zero_every_variant(cfg):
+    """K = 0 through each compiled GEMM variant: C = epilogue(bias) (no K step runs)."""
+    M, N = 37, 24
+    bias = workloads.random_matrix((N,), 56, "f16")
+    A = torch.zeros((M, 0), dtype=torch.float16)
+    B = torch.zeros((0, N), dtype=torch.float16)
+    for epi in ("none", "bias", "gelu"):
+        bb = bias if epi != "none" else None
+        C = _run(A, B, bb, epi, config_id=cfg)
+        y = oracle.gemm(A, B, bb, M, N, 0, "f16", epi)
+        assert_accept(to_f64(C), y, "f16", f"cfg{cfg} K=0 {epi}", small=True)
+
+
 def test_empty_outputs():
     for (M, N, K) in [(0, 64, 64), (64, 0, 64), (0, 0, 0)]:
         A = torch.zeros((M, K), dtype=torch.float16, device=DEV)
