@@ -123,7 +123,14 @@ def sweep(names, results_path, stream, log=print):
         out_f32 = w.epilogue == "softmax"
         C = torch.empty((w.M, w.N), dtype=torch.float32 if out_f32 else Ad.dtype, device=dev)
         kind = tg.TG_KERNEL_GEMM_SOFTMAX if out_f32 else tg.TG_KERNEL_GEMM
-        n = 20 if w.flops > 2 ** 38 else 100
+        # long graphs: in graphs of a few hundred launches a short kernel's
+        # dispatches were measured ~2.5 us longer than in graphs of 1000+
+        n = 20 if w.flops > 2 ** 38 else 1000
+        # let the clocks ramp up under load before the first candidate
+        t_warm = time.time() + 0.5
+        while time.time() < t_warm:
+            tg.gemm(Ad, Bd, bd, epilogue=w.epilogue, b_col_major=w.b_col_major, alpha=w.alpha, out=C)
+            torch.cuda.synchronize()
         rows = results.setdefault(name, {})
         for cid, gm, xcd in candidates(kind):
             key = f"{cid}/{gm}/{xcd}"
