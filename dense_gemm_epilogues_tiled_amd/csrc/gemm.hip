@@ -315,6 +315,7 @@ __global__ __launch_bounds__(2 * WM * WN * 64, 1) void gemm_ksplit_kernel(GemmPa
   constexpr int XBYTES = NS * 2 * H * FN * 1024;  // partial accumulators handed between the groups
   static_assert(STAGES >= 3 && LDS <= 160 * 1024 && (STAGES - 1) * DMA < 64, "ring");
   static_assert(FM % 2 == 0 && WTM % 16 == 0 && WTN % 16 == 0, "whole MFMA tiles, even row blocks");
+  static_assert(ORDER == 0 || FN % 2 == 0, "2x2 blocks of MFMA tiles");
   static_assert(XBYTES + BM * BN * 2 <= LDS, "partials and the C image fit in the ring");
 
   __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS];
