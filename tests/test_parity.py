@@ -89,6 +89,26 @@ def test_ragged_shapes_every_variant(cfg, dtype, b_col_major):
             assert_accept(to_f64(C), y, dtype, f"cfg{cfg} {dtype} {epi} {M}x{N}x{K}", small=True)
 
 
+@pytest.mark.parametrize("cfg", GEMM_IDS)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("b_col_major", [False, True])
+def test_long_k_every_variant(cfg, dtype, b_col_major):
+    """K = 1000: 16 K steps of 64 (32 of 32), so every variant's LDS ring wraps
+    several times, plus a 40-deep K tail; edge tiles in M and N."""
+    c = tg.configs()[cfg]
+    M, N, K = c["bm"] + 16, c["bn"] + 8, 1000
+    print(f"[parity] long K cfg={cfg} {dtype} bcol={b_col_major} M={M} N={N} K={K}", flush=True)
+    seed = 3000 + 10 * cfg
+    A = workloads.random_matrix((M, K), seed, dtype, scale=1 / 32)
+    B = workloads.random_matrix((N, K) if b_col_major else (K, N), seed + 1, dtype, scale=1 / 32)
+    bias = workloads.random_matrix((N,), seed + 2, dtype)
+    for epi in ("none", "gelu"):
+        bb = bias if epi != "none" else None
+        C = _run(A, B, bb, epi, b_col_major, config_id=cfg)
+        y = oracle.gemm(A, B, bb, M, N, K, dtype, epi, b_col_major=b_col_major)
+        assert_accept(to_f64(C), y, dtype, f"cfg{cfg} {dtype} {epi} {M}x{N}x{K}", small=True)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("b_col_major", [True, False])
 def test_softmax_shapes_every_variant(dtype, b_col_major):
