@@ -7,17 +7,15 @@ matrix cores.  One step = one launch of the fused kernel over one batch of
 resident inputs (the whole hot path: tile mapping, pipelined operand staging,
 MFMA main loop, register epilogue, single write of C).
 
-Timing: W eager warmup launches (default 2000, ~50 ms: the GPU clocks ramp up
-under load, so a short warmup under-reports the steady state), then K launches
-(default 2000, ~45 ms) captured in one HIP graph (replayed once untimed to
-upload it), then the timed region: one replay of the K-launch graph between
-torch.cuda.synchronize() calls.  In graphs of a few hundred launches each
-dispatch of this kernel was measured ~2.5 us longer than in graphs of 1000+
-launches or in CPU-paced eager launches, so K defaults to a long graph.  HIP events
-recorded on the launch stream around the same replay give the kernel's
-average duration for the roofline.  Inputs stay resident in HBM, so
-repeated launches see warm L2/MALL, as in the pages' warmup-then-average
-method.
+Timing: W eager warmup launches, then K launches captured in one HIP graph,
+which is replayed untimed until --warm-s seconds of wall time have passed
+(default 1 s: the GPU clocks ramp up under sustained load, and timing right
+after a short warmup under-reports the steady state), then the timed region:
+one more replay of the K-launch graph between torch.cuda.synchronize()
+calls.  HIP events recorded on the launch stream around the same replay give
+the kernel's average duration for the roofline.  The JSON line records the
+warm-up actually spent ("warm_s").  Inputs stay resident in HBM, so repeated
+launches see warm L2/MALL, as in the pages' warmup-then-average method.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -83,27 +81,49 @@ def measured_traffic(workload: str):
     return d.get("bytes_per_launch")
 
 
-def time_launches(launch, steps: int, warmup: int, stream, warm_ms: float = 0.0):
-    """Returns (wall ms per launch, event ms per launch).  At least `warmup`
-    launches, and more until `warm_ms` of wall time has passed (the GPU clocks
-    ramp up under sustained load)."""
-    import torch
-    t_end = time.perf_counter() + warm_ms * 1e-3
+def warm_by_wall_time(replay, sync, seconds: float, batch: int = 8):
+    """Replay `batch` times, synchronise, and repeat until `seconds` of wall
+    time have passed (at least one batch).  Keeps the GPU busy so its clocks
+    reach the level they hold under sustained load before anything is timed.
+    Returns (replays, seconds spent)."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(batch):
+            replay()
+            n += 1
+        sync()
+        spent = time.perf_counter() - t0
+        if spent >= seconds:
+            return n, spent
+
+
+def time_launches(launch, steps: int, warmup: int, stream, warm_s: float = 0.0, torch_mod=None):
+    """Time `steps` launches.  `warmup` eager launches, then the `steps`
+    launches are captured in one HIP graph, which is replayed untimed until
+    `warm_s` seconds of wall time have passed (at least once: that also
+    uploads it), then replayed once more between synchronisations (wall
+    clock) and HIP events recorded on the launch stream (kernel time).
+    Returns (wall ms per launch, event ms per launch, warm-up seconds)."""
+    torch = torch_mod
+    if torch is None:
+        import torch
     with torch.cuda.stream(stream):
         for _ in range(warmup):
             launch()
-        while warm_ms > 0 and time.perf_counter() < t_end:
-            for _ in range(10):
-                launch()
-            torch.cuda.synchronize()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         for _ in range(steps):
             launch()
-    with torch.cuda.stream(stream):
-        g.replay()  # upload, untimed
-    torch.cuda.synchronize()
+
+    def replay():
+        with torch.cuda.stream(stream):
+            g.replay()
+
+    # a long graph needs few replays per synchronisation; a short one more, so
+    # the queue stays ahead of the GPU
+    _, warm_spent = warm_by_wall_time(replay, torch.cuda.synchronize, warm_s, batch=max(1, min(64, 2000 // steps)))
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -114,15 +134,18 @@ def time_launches(launch, steps: int, warmup: int, stream, warm_ms: float = 0.0)
         e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
+    return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps, warm_spent
 
 
 def kernel_name(cfg: dict) -> str:
     """The kernel a tile configuration launches."""
     import dense_gemm_epilogues_tiled_amd as tg
     if cfg["kind"] == tg.TG_KERNEL_GEMM_SOFTMAX:
-        # the LDS-staged variants are built for column-major B only
-        return "gemm_softmax_lds_kernel" if cfg["b_col_major"] == 1 else "gemm_softmax_kernel"
+        if cfg["b_col_major"] != 1:
+            return "gemm_softmax_kernel"
+        # column-major-only variants: B staged through LDS in 32-deep steps, or
+        # held in registers in 64-deep chunks
+        return "gemm_softmax_reg_kernel" if cfg["bk"] == 64 else "gemm_softmax_lds_kernel"
     return "gemm_ksplit_kernel" if cfg["waves"] == 2 * cfg["wave_m"] * cfg["wave_n"] else "gemm_tile_kernel"
 
 
@@ -187,7 +210,7 @@ def bandwidth_table(dev, stream, names=None, steps=None, warmup: int = 10) -> di
                 def launch(ad=ad, w=w, out=out):
                     tg.row_softmax(ad, alpha=w.alpha, out=out)
             n = steps or (20 if w.min_bytes() > (1 << 30) else 100)
-            wall, ev = time_launches(launch, n, warmup, stream, warm_ms=150.0)
+            wall, ev, _ = time_launches(launch, n, warmup, stream, warm_s=0.15)
             gbs = w.min_bytes() / (ev * 1e-3) / 1e9
             table[name] = {"kernel": "vector_add_kernel" if w.kind == "vector_add" else "row_softmax_kernel",
                            "workload": w.description, "us": round(ev * 1e3, 3), "us_wall": round(wall * 1e3, 3),
@@ -220,7 +243,7 @@ def attention_table(dev, stream, names=None, steps=None, warmup: int = 5) -> dic
             def launch(q=q, k=k, v=v, w=w, out=out):
                 tg.attention(q, k, v, causal=w.causal, scale=w.scale, out=out)
             # long-running compute-bound kernel: give the clocks a full second
-            wall, ev = time_launches(launch, steps or 20, warmup, stream, warm_ms=1000.0)
+            wall, ev, _ = time_launches(launch, steps or 20, warmup, stream, warm_s=1.0)
             tf = w.flops / (ev * 1e-3) / 1e12
             table[name] = {"kernel": "attention_fwd_kernel", "workload": w.description, "us": round(ev * 1e3, 3),
                            "us_wall": round(wall * 1e3, 3), "algorithmic_flops": w.flops, "TFLOP/s": round(tf, 1),
@@ -234,13 +257,15 @@ def attention_table(dev, stream, names=None, steps=None, warmup: int = 5) -> dic
     return table
 
 
-def main() -> int:
+def build_parser() -> argparse.ArgumentParser:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=2000,
-                    help="untimed launches before the timed region (about 50 ms at the headline shape, "
-                         "enough for the GPU clocks to settle)")
+                    help="untimed eager launches before the graph is captured")
+    ap.add_argument("--warm-s", type=float, default=1.0,
+                    help="seconds of untimed graph replays right before the timed replay (the GPU clocks settle "
+                         "under sustained load)")
     ap.add_argument("--workload", default=HEADLINE,
                     help="GEMM workload to time (default: the headline); a bandwidth (V1, V2, S1) or attention "
                          "(A1, A2) workload name times that kernel alone and prints its entry (for profiling runs)")
@@ -249,7 +274,11 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before timing, copy a MIB-sized buffer 3 times (a plain copy kernel of known size "
                          "whose FETCH_SIZE / WRITE_SIZE counters calibrate HBM traffic readings)")
-    args = ap.parse_args()
+    return ap
+
+
+def main() -> int:
+    args = build_parser().parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -304,7 +333,7 @@ def main() -> int:
         tg.gemm(Ad, Bd, bd, epilogue=w.epilogue, b_col_major=w.b_col_major, alpha=w.alpha, out=Cd)
 
     log(f"timing {w.name}: {w.description}; warmup {args.warmup}, steps {args.steps}")
-    ms_wall, ms_kernel = time_launches(launch, args.steps, args.warmup, stream)
+    ms_wall, ms_kernel, warm_spent = time_launches(launch, args.steps, args.warmup, stream, warm_s=args.warm_s)
     tflops = w.flops / (ms_wall * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     achieved = w.flops / (ms_kernel * 1e-3) / 1e12
@@ -324,6 +353,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warm_s": round(warm_spent, 3),
         "ms_per_step": ms_wall,
         "higher_is_better": True,
         "scaling": "weak",
@@ -354,7 +384,7 @@ def main() -> int:
                     tg.gemm(At, Bt, bt, epilogue=wt.epilogue, b_col_major=wt.b_col_major, alpha=wt.alpha, out=Ct)
 
                 n = 50 if wt.M * wt.N * wt.K > 2 ** 36 else 1000
-                wall, ev = time_launches(lt, n, 10, stream, warm_ms=150.0)
+                wall, ev, _ = time_launches(lt, n, 10, stream, warm_s=args.warm_s)
                 tf = wt.flops / (ev * 1e-3) / 1e12
                 gbs = wt.min_bytes() / (ev * 1e-3) / 1e9
                 table[name] = {"us": round(ev * 1e3, 3), "us_wall": round(wall * 1e3, 3), "TFLOP/s": round(tf, 1),

@@ -111,11 +111,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // ... lds): lane i's bytes land at LDS address m0 + 16 i.  Out-of-range
 // offsets (kOOB) write zeros.  Issued as inline asm so the compiler does not
 // model these LDS writes: completion is tracked explicitly with vmcnt waits
-// before the barrier that publishes a stage.
+// before the barrier that publishes a stage.  gfx950 needs one wait state
+// between a scalar write of M0 and an LDS DMA that reads it; the compiler's
+// hazard pass cannot see into the asm string, so the s_nop is written here
+// (it is what the compiler itself emits around its own LDS-DMA builtin).
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_base_uniform, int voff) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(lds_base_uniform), "v"(voff), "s"(r)
                : "memory", "m0");

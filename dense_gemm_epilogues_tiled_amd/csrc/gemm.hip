@@ -28,8 +28,11 @@
 //     output type and writes C once.
 
 #include "gemm_common.hpp"
+#include "phases.hpp"
 
 namespace tg {
+
+TG_PHASE_BUFFER(gemm)
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, bool B_COL>
 struct GemmShape {
@@ -62,6 +65,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
 
   __shared__ __attribute__((aligned(1024))) unsigned char smem[S::LDS];
 
+  TG_PHASE_DECL;
+  TG_PHASE(0);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -194,11 +199,13 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s) issue_stage(s, s);
   }
+  TG_PHASE(1);
   if (KT > 0) {
     if constexpr (KK == 2)
       wait_vm_barrier<(STAGES - 2) * S::DMA + COPIES_B>();
     else
       wait_vm_barrier<(STAGES - 2) * S::DMA>();
+    TG_PHASE(2);
     load_frags(0, 0, F0);
     if constexpr (KK == 2) {
       // Explicitly interleaved K step (two 32-deep slices):
@@ -268,12 +275,18 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64, 1) void gemm_tile_kernel(Gem
   // through an LDS image of the tile.  Copies issued past the end of K may
   // still be writing LDS; once every wave is past the barrier the ring is
   // free for the image.
+  TG_PHASE(3);
   with_epilogue(p.epilogue, [&](auto epi_c) {
     u32x2 out[FM][FN];
     finish_tile<decltype(epi_c)::value, DT>(p, acc, out, n0, wn * S::WTN, fk);
+    TG_PHASE(4);
     wait_vm_barrier<0>();
+    TG_PHASE(5);
     store_tile_staged<DT, BM, BN, S::NT, FM, FN>(p, out, smem, m0, n0, wm * S::WTM, wn * S::WTN, fr, fk, tid);
   });
+  TG_PHASE(6);
+  TG_PHASE_DRAINED(7);
+  TG_PHASE_WRITE(gemm);
 }
 
 // ---------------------------------------------------------------------------
@@ -320,6 +333,8 @@ __global__ __launch_bounds__(2 * WM * WN * 64, 1) void gemm_ksplit_kernel(GemmPa
 
   __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS];
 
+  TG_PHASE_DECL;
+  TG_PHASE(0);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -411,8 +426,10 @@ __global__ __launch_bounds__(2 * WM * WN * 64, 1) void gemm_ksplit_kernel(GemmPa
 
 #pragma unroll
   for (int st = 0; st < STAGES - 1; ++st) issue_stage(st, st);
+  TG_PHASE(1);
   if (KT > 0) {
     wait_vm_barrier<(STAGES - 2) * DMA>();
+    TG_PHASE(2);
     {
       const unsigned char* sA = smem;
 #pragma unroll
@@ -431,6 +448,7 @@ __global__ __launch_bounds__(2 * WM * WN * 64, 1) void gemm_ksplit_kernel(GemmPa
   }
   // every copy landed and every wave is done with the ring
   wait_vm_barrier<0>();
+  TG_PHASE(3);
 
   // ---- sum the two groups' partials, then the epilogue: group g finishes
   // row blocks [H g, H g + H) of its output block.  The tile goes out in H
@@ -454,6 +472,7 @@ __global__ __launch_bounds__(2 * WM * WN * 64, 1) void gemm_ksplit_kernel(GemmPa
       for (int i = 0; i < H; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[H * G + i][j] += xbuf[xidx(G, i, j)];
+      TG_PHASE(4);
       static_for<H>([&](auto ih_c) {
         constexpr int IH = decltype(ih_c)::value;
 #pragma unroll
@@ -477,6 +496,7 @@ __global__ __launch_bounds__(2 * WM * WN * 64, 1) void gemm_ksplit_kernel(GemmPa
           const u32x4 val = *reinterpret_cast<const u32x4*>(cimg + c_image_off<BN>(r, 2 * v));
           if (m < M && n < N) *reinterpret_cast<u32x4*>(gC + (size_t)m * N + n) = val;
         }
+        if constexpr (IH == 0) TG_PHASE(5);
       });
     };
     if (g == 0)
@@ -484,6 +504,9 @@ __global__ __launch_bounds__(2 * WM * WN * 64, 1) void gemm_ksplit_kernel(GemmPa
     else
       finish(std::integral_constant<int, 1>{});
   });
+  TG_PHASE(6);
+  TG_PHASE_DRAINED(7);
+  TG_PHASE_WRITE(gemm);
 }
 
 // ---------------------------------------------------------------------------

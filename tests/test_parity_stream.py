@@ -71,9 +71,9 @@ def test_vector_add_workload_2p22():
 
 
 def test_vector_add_workload_2p28_sampled():
-    """The 3 GiB case: every element is computed by the grid-stride loop many
-    trips deep; 65,536 seeded positions are checked (the operation is
-    elementwise, so the oracle sees just those pairs)."""
+    """The 3 GiB case: 2^26 threads of 16-byte vectors, so the grid's block
+    index runs into the millions; 65,536 seeded positions are checked (the
+    operation is elementwise, so the oracle sees just those pairs)."""
     w = workloads.STREAM_WORKLOADS["V2"]
     print(f"[parity] V2: {w.description}", flush=True)
     A, B = workloads.make_stream_inputs(w)
@@ -116,7 +116,8 @@ def _near_patterns(n: int, dtype: str, seed: int):
 @pytest.mark.parametrize("n", [1, 7, 8, 9, 4093, 100_003, (1 << 21) + 5])
 def test_vector_add_every_bit_pattern_class(dtype, n):
     """Random bit patterns at lengths around the 16-byte vector and the
-    grid-stride trip: the vector body, the remainder loop and the scalar tail."""
+    256-thread block: whole vectors, a partly filled last block and the
+    elements past the last whole vector, which go one per thread."""
     print(f"[parity] vector_add {dtype} n={n} random patterns", flush=True)
     A = _random_patterns(n, dtype, 10 + n % 97)
     B = _random_patterns(n, dtype, 20 + n % 89)
