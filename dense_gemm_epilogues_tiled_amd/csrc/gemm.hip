@@ -494,7 +494,7 @@ __global__ __launch_bounds__(2 * WM * WN * 64, 1) void gemm_ksplit_kernel(GemmPa
           const int r = (rr / 16) * (16 * H) + 16 * IH + rr % 16;
           const int m = m0 + r, n = n0 + 8 * v;
           const u32x4 val = *reinterpret_cast<const u32x4*>(cimg + c_image_off<BN>(r, 2 * v));
-          if (m < M && n < N) *reinterpret_cast<u32x4*>(gC + (size_t)m * N + n) = val;
+          if (m < M && n < N) store_nt(reinterpret_cast<u32x4*>(gC + (size_t)m * N + n), val);
         }
         if constexpr (IH == 0) TG_PHASE(5);
       });

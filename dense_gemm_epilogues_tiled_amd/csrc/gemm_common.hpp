@@ -258,6 +258,8 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams& p, const u32
     const int r = q / PIECES_PER_ROW, v = q % PIECES_PER_ROW;
     const int m = m0 + r, n = n0 + 8 * v;
     const u32x4 val = *reinterpret_cast<const u32x4*>(smem + c_image_off<BN>(r, 2 * v));
+    // plain stores: for this kernel non-temporal ones measured the same at
+    // 8192^3 and 4.6% slower at 3000 x 5000 x 1000 (one tile per CU)
     if (m < M && n < N) *reinterpret_cast<u32x4*>(gC + (size_t)m * N + n) = val;
   }
 }

@@ -335,7 +335,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_softmax_lds_kernel(Softmax
     const int r = q * RPI + lane / LPR;
     const int c4 = lane % LPR;
     const f32x4 v = *reinterpret_cast<const f32x4*>(wreg + r * OUT_STRIDE + c4 * 16);
-    if (m0 + r < M && 4 * c4 < cols) *reinterpret_cast<f32x4*>(p.C + (size_t)(m0 + r) * N + col0 + 4 * c4) = v;
+    if (m0 + r < M && 4 * c4 < cols) store_nt(reinterpret_cast<f32x4*>(p.C + (size_t)(m0 + r) * N + col0 + 4 * c4), v);
   }
   TG_PHASE(6);
   TG_PHASE_DRAINED(7);
@@ -496,8 +496,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_softmax_reg_kernel(Softmax
     for (int j = 0; j < PIECES; ++j) {
       const int col = 256 * j + 4 * lane;
       if (col < N)
-        __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&stage[r * ROW + col]),
-                                    reinterpret_cast<f32x4*>(crow + col));
+        store_nt(reinterpret_cast<f32x4*>(crow + col), *reinterpret_cast<const f32x4*>(&stage[r * ROW + col]));
     }
   }
   TG_PHASE(6);
