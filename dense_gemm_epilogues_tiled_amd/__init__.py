@@ -46,6 +46,7 @@ TG_KERNEL_GEMM_SOFTMAX = 1
 TG_SOFTMAX_MAX_N = 2048
 TG_ROW_SOFTMAX_MAX_ROW_BYTES = 16384
 TG_ATTN_MAX_SEQ = 1 << 20
+TG_AUTOTUNE_NOALLOC_MAX_BYTES = 32 * 1024 * 1024 + 8192
 
 EPILOGUES = {
     "none": TG_EPI_NONE, "bias": TG_EPI_BIAS, "relu": TG_EPI_BIAS_RELU, "bias_relu": TG_EPI_BIAS_RELU,
@@ -103,6 +104,8 @@ _SIGNATURES = {
                                                        ctypes.POINTER(ctypes.c_int64)]),
     "tg_gemm_autotune": (ctypes.c_int, [ctypes.POINTER(tg_gemm_args), ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                         ctypes.POINTER(tg_autotune_entry), ctypes.c_void_p]),
+    "tg_gemm_autotune_noalloc": (ctypes.c_int, [ctypes.POINTER(tg_gemm_args), ctypes.c_int,
+                                                ctypes.POINTER(tg_autotune_entry), ctypes.c_void_p]),
     "tg_autotune_cache_size": (ctypes.c_int, []),
     "tg_autotune_cache_get": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(tg_autotune_entry)]),
     "tg_autotune_cache_clear": (ctypes.c_int, []),
@@ -359,6 +362,14 @@ def attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, causal: bool = 
     if rc != TG_OK:
         raise TgError(rc, "tg_attention_fwd")
     return out
+
+
+def tg_gemm_autotune_noalloc(args: tg_gemm_args | None, iters: int, stream: int | None):
+    """Returns (status, tg_autotune_entry)."""
+    res = tg_autotune_entry()
+    rc = load().tg_gemm_autotune_noalloc(ctypes.byref(args) if args is not None else None, iters, ctypes.byref(res),
+                                         stream)
+    return rc, res
 
 
 def autotune(A: torch.Tensor, B: torch.Tensor, bias: torch.Tensor | None = None, epilogue: str = "none",

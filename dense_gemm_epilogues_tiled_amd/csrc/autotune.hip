@@ -84,16 +84,19 @@ __global__ __launch_bounds__(256) void count_mismatch_kernel(const void* c, cons
   if (threadIdx.x == 0) partial[blockIdx.x] = red[0];
 }
 
+// Reads of the GPU's constant 100 MHz clock, in stream order: one thread
+// writes the counter (vector store) where the host asked.  Two such reads
+// around a candidate's launches time them without HIP events (whose creation
+// allocates).
+__global__ __launch_bounds__(64) void clock_stamp_kernel(unsigned long long* out) {
+  const unsigned long long t = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) out[0] = t;
+}
+
 int64_t out_bytes(int64_t M, int64_t N, int epilogue) { return M * N * (epilogue == TG_EPI_SOFTMAX ? 4 : 2); }
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
-
-struct Events {
-  hipEvent_t a = nullptr, b = nullptr;
-  ~Events() {
-    if (a) (void)hipEventDestroy(a);
-    if (b) (void)hipEventDestroy(b);
-  }
-};
+// workspace layout: reference output | kCmpBlocks mismatch counts | 2 clock stamps
+constexpr int64_t kTailBytes = kCmpBlocks * sizeof(unsigned) + 256;
 
 }  // namespace
 
@@ -119,23 +122,34 @@ extern "C" {
 
 int tg_gemm_autotune_workspace_size(int64_t M, int64_t N, int epilogue, int64_t* bytes) {
   if (!bytes || M < 0 || N < 0 || epilogue < TG_EPI_NONE || epilogue > TG_EPI_SOFTMAX) return TG_ERR_INVALID_ARG;
-  *bytes = align256(out_bytes(M, N, epilogue)) + kCmpBlocks * (int64_t)sizeof(unsigned);
+  *bytes = align256(out_bytes(M, N, epilogue)) + kTailBytes;
   return TG_OK;
 }
 
-int tg_gemm_autotune(const tg_gemm_args* args, void* workspace, int64_t workspace_bytes, int iters,
-                     tg_autotune_entry* result, void* stream) {
+}  // extern "C"
+
+namespace tg {
+namespace {
+
+// Argument checks shared by both entry points (no HIP call); *need receives
+// the workspace bytes the problem takes.
+int autotune_check(const tg_gemm_args* args, int iters, const tg_autotune_entry* result, int64_t* need) {
   if (!args || !result || iters < 1 || iters > 1000) return TG_ERR_INVALID_ARG;
   tg_tile_config probe;
   int rc = tg_gemm_query_config(args->M, args->N, args->K, args->dtype, args->epilogue, args->b_col_major, &probe);
   if (rc != TG_OK) return rc;
-  const int kind = args->epilogue == TG_EPI_SOFTMAX ? TG_KERNEL_GEMM_SOFTMAX : TG_KERNEL_GEMM;
-  int64_t need = 0;
-  rc = tg_gemm_autotune_workspace_size(args->M, args->N, args->epilogue, &need);
+  rc = tg_gemm_autotune_workspace_size(args->M, args->N, args->epilogue, need);
   if (rc != TG_OK) return rc;
   if (args->M == 0 || args->N == 0) return TG_ERR_INVALID_ARG;  // nothing to time
-  if (!workspace || workspace_bytes < need) return TG_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return TG_ERR_MISALIGNED;
+  return TG_OK;
+}
+
+// The search, on a checked problem, with `workspace` (256-byte aligned, at
+// least the problem's workspace size) for the reference output, the
+// mismatch counts and the clock stamps.
+int autotune_run(const tg_gemm_args* args, void* workspace, int iters, tg_autotune_entry* result, void* stream) {
+  int rc;
+  const int kind = args->epilogue == TG_EPI_SOFTMAX ? TG_KERNEL_GEMM_SOFTMAX : TG_KERNEL_GEMM;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   // the reference: the default choice (baked table / rule), written to the workspace
@@ -154,11 +168,10 @@ int tg_gemm_autotune(const tg_gemm_args* args, void* workspace, int64_t workspac
   const float tol = args->epilogue == TG_EPI_SOFTMAX ? 1e-4f : 1e-2f;
   unsigned* partial = reinterpret_cast<unsigned*>(static_cast<unsigned char*>(workspace) +
                                                   align256(out_bytes(args->M, args->N, args->epilogue)));
+  unsigned long long* stamps = reinterpret_cast<unsigned long long*>(partial + kCmpBlocks);
   const int cmp_blocks = (int)(n_out / 2048 + 1 < kCmpBlocks ? n_out / 2048 + 1 : kCmpBlocks);
-  std::vector<unsigned> host_partial(cmp_blocks);
-
-  Events ev;
-  if (hipEventCreate(&ev.a) != hipSuccess || hipEventCreate(&ev.b) != hipSuccess) return TG_ERR_HIP;
+  unsigned host_partial[kCmpBlocks];
+  unsigned long long host_stamps[2];
 
   static const int kGroups[] = {1, 4, 8, 16};
   tg_gemm_args best = *args;
@@ -180,22 +193,24 @@ int tg_gemm_autotune(const tg_gemm_args* args, void* workspace, int64_t workspac
         hipLaunchKernelGGL(count_mismatch_kernel, dim3(cmp_blocks), dim3(256), 0, s, args->C, workspace, n_out,
                            out_kind, tol, tol, partial);
         if (hipGetLastError() != hipSuccess) return TG_ERR_HIP;
-        if (hipMemcpyAsync(host_partial.data(), partial, cmp_blocks * sizeof(unsigned), hipMemcpyDeviceToHost, s) !=
+        if (hipMemcpyAsync(host_partial, partial, cmp_blocks * sizeof(unsigned), hipMemcpyDeviceToHost, s) !=
                 hipSuccess ||
             hipStreamSynchronize(s) != hipSuccess)
           return TG_ERR_HIP;
         uint64_t bad = 0;
-        for (unsigned v : host_partial) bad += v;
+        for (int b = 0; b < cmp_blocks; ++b) bad += host_partial[b];
         if (bad != 0) continue;
         ++valid;
-        // time: one more warm launch, then `iters` launches between events
+        // time: one more warm launch, then `iters` launches between two clock stamps
         if (tg_gemm_ex(&c, stream) != TG_OK) continue;
-        if (hipEventRecord(ev.a, s) != hipSuccess) return TG_ERR_HIP;
+        hipLaunchKernelGGL(clock_stamp_kernel, dim3(1), dim3(64), 0, s, stamps);
         for (int i = 0; i < iters; ++i) (void)tg_gemm_ex(&c, stream);
-        if (hipEventRecord(ev.b, s) != hipSuccess || hipEventSynchronize(ev.b) != hipSuccess) return TG_ERR_HIP;
-        float ms = 0.f;
-        if (hipEventElapsedTime(&ms, ev.a, ev.b) != hipSuccess) return TG_ERR_HIP;
-        const float us = ms * 1000.f / iters;
+        hipLaunchKernelGGL(clock_stamp_kernel, dim3(1), dim3(64), 0, s, stamps + 1);
+        if (hipGetLastError() != hipSuccess ||
+            hipMemcpyAsync(host_stamps, stamps, sizeof host_stamps, hipMemcpyDeviceToHost, s) != hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess)
+          return TG_ERR_HIP;
+        const float us = (float)(host_stamps[1] - host_stamps[0]) * 0.01f / iters;  // 100 MHz ticks
         if (best_us < 0.f || us < best_us) {
           best_us = us;
           best = c;
@@ -225,6 +240,79 @@ int tg_gemm_autotune(const tg_gemm_args* args, void* workspace, int64_t workspac
   rc = tg_gemm_ex(&best, stream);
   if (rc != TG_OK) return rc;
   return hipStreamSynchronize(s) == hipSuccess ? TG_OK : TG_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace tg
+
+extern "C" {
+
+int tg_gemm_autotune(const tg_gemm_args* args, void* workspace, int64_t workspace_bytes, int iters,
+                     tg_autotune_entry* result, void* stream) {
+  int64_t need = 0;
+  const int rc = autotune_check(args, iters, result, &need);
+  if (rc != TG_OK) return rc;
+  if (!workspace || workspace_bytes < need) return TG_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return TG_ERR_MISALIGNED;
+  return autotune_run(args, workspace, iters, result, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant: the workspace is a fixed device array of this
+// library, TG_AUTOTUNE_NOALLOC_MAX_BYTES long, which every GPU the library
+// runs on holds until the process ends.  Host code never passes the array's
+// name to a kernel or a copy (on the host it is only a stand-in): the first
+// call on a device, with that device current, asks the runtime for the
+// array's device address on that device and keeps it.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[TG_AUTOTUNE_NOALLOC_MAX_BYTES];
+
+namespace tg {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // device address of `scratch` on each device, once looked up
+
+// The current device's copy of the scratch array, or NULL (status in *rc).
+void* scratch_address(int* rc) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    *rc = TG_ERR_HIP;
+    return nullptr;
+  }
+  if (dev >= kMaxDevices) {
+    *rc = TG_ERR_UNSUPPORTED;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      *rc = TG_ERR_HIP;
+      return nullptr;
+    }
+    g_scratch[dev] = p;
+  }
+  *rc = TG_OK;
+  return g_scratch[dev];
+}
+
+}  // namespace
+}  // namespace tg
+
+extern "C" {
+
+int tg_gemm_autotune_noalloc(const tg_gemm_args* args, int iters, tg_autotune_entry* result, void* stream) {
+  int64_t need = 0;
+  int rc = autotune_check(args, iters, result, &need);
+  if (rc != TG_OK) return rc;
+  if (need > (int64_t)TG_AUTOTUNE_NOALLOC_MAX_BYTES) return TG_ERR_UNSUPPORTED;
+  void* ws = scratch_address(&rc);
+  if (!ws) return rc;
+  return autotune_run(args, ws, iters, result, stream);
 }
 
 int tg_autotune_cache_size(void) {

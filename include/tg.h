@@ -38,12 +38,17 @@
  *           TG_EPI_SOFTMAX    C_ij = exp(x_ij - max_j x_ij) / sum_j exp(...)
  *                             (bias must be NULL; row length N <= TG_SOFTMAX_MAX_N)
  *  Memory   Every pointer is a device pointer owned by the caller.  The library
- *           never allocates or frees device memory; apart from the autotuner
- *           (tg_gemm_autotune, which times candidates and waits for them) it
- *           never synchronises and only enqueues one kernel on `stream` (a
- *           hipStream_t; NULL = the null stream).  Its only mutable state is
- *           the autotune cache, guarded by a lock, so concurrent calls from
- *           several host threads are safe.  C must not overlap A, B or bias.
+ *           never allocates or frees device memory (its one device array of
+ *           its own, the workspace of tg_gemm_autotune_noalloc, comes with its
+ *           device code, as a static variable); apart from the autotuners
+ *           (tg_gemm_autotune and tg_gemm_autotune_noalloc, which time
+ *           candidates and wait for them) it never synchronises and only
+ *           enqueues one kernel on `stream` (a hipStream_t; NULL = the null
+ *           stream).  Its mutable state is the autotune cache, guarded by a
+ *           lock, so concurrent calls from several host threads are safe, and
+ *           the workspace array of tg_gemm_autotune_noalloc (concurrent calls
+ *           of that one entry point on one GPU race; see there).  C must not
+ *           overlap A, B or bias.
  *  Errors   Every entry point returns a tg_status.  All argument checks run on
  *           the host before any HIP call, so an invalid call touches no device
  *           and enqueues nothing.  A launch failure reported by the runtime
@@ -289,7 +294,8 @@ typedef struct tg_autotune_entry {
 } tg_autotune_entry;
 
 /* Bytes of device workspace tg_gemm_autotune needs for an M x N output with
- * this epilogue (a copy of the reference output plus 4 KiB of counters). */
+ * this epilogue (a copy of the reference output, 4 KiB of mismatch counters
+ * and 256 bytes for two clock stamps). */
 int tg_gemm_autotune_workspace_size(int64_t M, int64_t N, int epilogue, int64_t* bytes);
 
 /*
@@ -304,8 +310,9 @@ int tg_gemm_autotune_workspace_size(int64_t M, int64_t N, int epilogue, int64_t*
  * candidate's C is compared on the device element by element (|c - r| <=
  * 1e-2 + 1e-2 |r| for fp16 / bf16 outputs, 1e-4 + 1e-4 |r| for the fp32
  * softmax; non-finite values must agree).  Each valid candidate is timed over
- * `iters` launches (1 .. 1000) between HIP events on `stream`.  The call
- * blocks until the search is done.
+ * `iters` launches (1 .. 1000) on `stream`, between two reads of the GPU's
+ * constant 100 MHz clock that a one-thread kernel writes into the workspace
+ * in stream order.  The call blocks until the search is done.
  * Returns TG_OK; the argument errors of tg_gemm_ex; TG_ERR_INVALID_ARG for
  * NULL args / result, iters out of range, an empty output (M or N zero) or a
  * missing / short workspace; TG_ERR_MISALIGNED for a misaligned workspace;
@@ -314,6 +321,33 @@ int tg_gemm_autotune_workspace_size(int64_t M, int64_t N, int epilogue, int64_t*
  */
 int tg_gemm_autotune(const tg_gemm_args* args, void* workspace, int64_t workspace_bytes, int iters,
                      tg_autotune_entry* result, void* stream);
+
+/* Largest workspace tg_gemm_autotune_noalloc can use: 32 MiB + 8 KiB, i.e.
+ * outputs up to 32 MiB (16 Mi fp16 / bf16 or 8 Mi fp32 values). */
+#define TG_AUTOTUNE_NOALLOC_MAX_BYTES (32 * 1024 * 1024 + 8192)
+
+/*
+ * tg_gemm_autotune_noalloc -- tg_gemm_autotune for callers that cannot
+ * allocate device memory (code under HIP graph capture rules, tight serving
+ * loops, harnesses that forbid hipMalloc): the same search, with the
+ * workspace taken from a fixed device array inside the library instead of
+ * the caller.  It calls no hipMalloc, hipFree or other allocating routine.
+ *
+ *  Scratch  TG_AUTOTUNE_NOALLOC_MAX_BYTES of device memory per GPU the
+ *           library runs on, held until the process ends.  Its device
+ *           address on a GPU is looked up on the first call made with that
+ *           GPU current.  Every call on one GPU shares that GPU's array and
+ *           overwrites it; calls that overlap on one GPU (several host
+ *           threads or streams at once) race and must not be made.
+ *  Args     as tg_gemm_autotune without the workspace: args (its config_id,
+ *           group_m and xcd_remap ignored), iters 1 .. 1000, result.
+ *  Errors   the argument errors of tg_gemm_autotune; TG_ERR_UNSUPPORTED when
+ *           the problem's workspace (tg_gemm_autotune_workspace_size)
+ *           exceeds TG_AUTOTUNE_NOALLOC_MAX_BYTES or no candidate ran and
+ *           matched; TG_ERR_HIP if the runtime cannot give the array's
+ *           address or a launch / copy fails.
+ */
+int tg_gemm_autotune_noalloc(const tg_gemm_args* args, int iters, tg_autotune_entry* result, void* stream);
 
 /* Number of cached entries; entry `index` (TG_ERR_INVALID_ARG if out of
  * range or out is NULL); forget every entry. */
