@@ -141,11 +141,8 @@ def kernel_name(cfg: dict) -> str:
     """The kernel a tile configuration launches."""
     import dense_gemm_epilogues_tiled_amd as tg
     if cfg["kind"] == tg.TG_KERNEL_GEMM_SOFTMAX:
-        if cfg["b_col_major"] != 1:
-            return "gemm_softmax_kernel"
-        # column-major-only variants: B staged through LDS in 32-deep steps, or
-        # held in registers in 64-deep chunks
-        return "gemm_softmax_reg_kernel" if cfg["bk"] == 64 else "gemm_softmax_lds_kernel"
+        # the LDS-staged variants are built for column-major B only
+        return "gemm_softmax_lds_kernel" if cfg["b_col_major"] == 1 else "gemm_softmax_kernel"
     return "gemm_ksplit_kernel" if cfg["waves"] == 2 * cfg["wave_m"] * cfg["wave_n"] else "gemm_tile_kernel"
 
 

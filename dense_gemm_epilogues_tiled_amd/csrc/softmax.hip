@@ -197,15 +197,27 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_softmax_kernel(SoftmaxPara
 // own copy of the 16 x 32 A step.  No LDS is shared between waves during the
 // product, so no workgroup barrier is needed there.  LDS rows are 64 bytes
 // (32 k), 16-byte chunks XOR-swizzled by (row / 4) % 4 so 16 consecutive rows
-// at one chunk hit 16 distinct slots.  The softmax result is staged back
-// through the same region so each store instruction writes two contiguous
-// 512-byte row segments.
+// at one chunk hit 16 distinct slots.  The row softmax takes one workgroup
+// barrier (per-wave (max, sum) pairs, combined after it).  The result is
+// staged back through the same region so each store instruction writes two
+// contiguous 512-byte row segments, non-temporal.
+// Keeping B in registers instead (every operand of the wave's product loaded
+// at once, the row assembled in LDS and stored as whole rows) measured
+// slower: 13.5 us against 10.8 us at 4096 x 1024 x 128, its loads of the
+// whole of B into 256 workgroups' registers arriving at half the rate of
+// these copies.
 // ---------------------------------------------------------------------------
-template <int WAVES, int NSUB, class DT>
+// FULL_LINES: 64-deep K steps instead of 32-deep ones, one step in flight
+// per wave (the same LDS as two 32-deep steps): each copy then reads whole
+// 128-byte lines (8 rows x 128 bytes) instead of half lines (16 rows x 64
+// bytes, the other halves read by the next step's copies).
+template <int WAVES, int NSUB, bool FULL_LINES, class DT>
 __global__ __launch_bounds__(WAVES * 64, 1) void gemm_softmax_lds_kernel(SoftmaxParams p) {
-  constexpr int SLOT = (1 + NSUB) * 1024;  // one K step: A (16 rows) + NSUB x 16 B rows, 64 B each
-  constexpr int WREG = 2 * SLOT;           // two steps in flight per wave
-  constexpr int DMA = 1 + NSUB;            // 1 KB copies per wave per step
+  constexpr int BKS = FULL_LINES ? 64 : 32;           // K per step
+  constexpr int SLOT = (1 + NSUB) * 16 * BKS * 2;     // one K step: A (16 rows) + NSUB x 16 B rows
+  constexpr int NSLOT = FULL_LINES ? 1 : 2;           // steps in flight per wave
+  constexpr int WREG = NSLOT * SLOT;
+  constexpr int DMA = SLOT / 1024;                    // 1 KB copies per wave per step
   constexpr int OUT_STRIDE = NSUB * 64 + 16;  // staged output row (floats of 16 columns x NSUB), padded
   static_assert(16 * OUT_STRIDE <= WREG, "output staging fits the wave region");
   static_assert(WAVES * WREG + 2 * WAVES * 16 * 4 <= 160 * 1024, "LDS of one CU");
@@ -222,7 +234,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_softmax_lds_kernel(Softmax
   const int M = p.M, N = p.N, K = p.K;
   const int n_sub = p.n_sub;
   const int m0 = blockIdx.x * 16;
-  const int col0 = wave * n_sub * 16;
+  // column block of this wave, rotated by workgroup so that the workgroups
+  // running at the same time read different parts of B (measured 1.7% faster
+  // on 4096 x 1024 x 128 than every workgroup reading B in the same order)
+  const int col0 = ((wave + (int)blockIdx.x) % WAVES) * n_sub * 16;
 
   const uint16_t* __restrict__ gA = static_cast<const uint16_t*>(p.A);
   const uint16_t* __restrict__ gB = static_cast<const uint16_t*>(p.B);
@@ -231,96 +246,139 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_softmax_lds_kernel(Softmax
   unsigned char* wreg = smem + wave * WREG;
   const uint32_t wbase = lds_addr(wreg);
 
-  // Copy plan of one step: copy j (0 = A, 1 + s = B tile s) lane i fills LDS
-  // row 16 j' + i/4 (j' = 0 for A, s for B), physical slot i % 4, i.e. logical
-  // chunk (i % 4) ^ (i / 16); its global source is that row's 8 k values.
-  const int crow = lane >> 2;
-  const int cchunk = (lane & 3) ^ (lane >> 4);
-  const bool a_ok = (m0 + crow) < M;
+  // Copy plan of one step, in the kc_off<BKS> layout (rows of 2 BKS bytes):
+  // each 1 KB copy covers RPC = 64 / CPR rows; lane i fills the 16-byte
+  // slot i % CPR of row i / CPR of its copy, i.e. logical chunk
+  // (i % CPR) ^ ((row / (16 / CPR)) % CPR); its global source is that row's
+  // 8 k values.  Copies 0 .. CA-1 hold the 16 A rows, then CB per B tile.
+  constexpr int CPR = BKS / 8;         // 16-byte chunks per row
+  constexpr int RPC = 64 / CPR;        // rows per 1 KB copy
+  constexpr int CA = 16 / RPC;         // copies per 16 rows
+  const int crow = lane / CPR;
+  auto cchunk = [&](int row) { return (lane % CPR) ^ ((row / (16 / CPR)) % CPR); };
   auto issue_step = [&](int kb, int slot) {
-    const int k = kb * 32 + cchunk * 8;
-    const bool k_ok = k < K;
     const uint32_t sb = wbase + slot * SLOT;
-    dma16(rA, sb, (a_ok && k_ok) ? (crow * K + k) * 2 : kOOB);
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      const int nl = 16 * s + crow;
-      const bool ok = k_ok && s < n_sub && (col0 + nl) < N;
-      dma16(rB, sb + 1024 * (1 + s), ok ? (nl * K + k) * 2 : kOOB);
+    for (int c = 0; c < CA; ++c) {
+      const int row = RPC * c + crow;  // of the 16 A rows
+      const int k = kb * BKS + cchunk(row) * 8;
+      dma16(rA, sb + 1024 * c, ((m0 + row) < M && k < K) ? (row * K + k) * 2 : kOOB);
     }
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+      for (int c = 0; c < CA; ++c) {
+        const int row = RPC * c + crow;  // of B tile s
+        const int nl = 16 * s + row;
+        const int k = kb * BKS + cchunk(row) * 8;
+        const bool ok = k < K && s < n_sub && (col0 + nl) < N;
+        dma16(rB, sb + 1024 * (CA * (1 + s) + c), ok ? (nl * K + k) * 2 : kOOB);
+      }
   };
 
   f32x4 acc[NSUB];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int KB = (K + 31) / 32;
-  issue_step(0, 0);
-  issue_step(1, 1);
-  TG_PHASE(1);
-  for (int kb = 0; kb < KB; ++kb) {
-    const int slot = kb & 1;
-    // step kb is complete once only step kb+1's copies are in flight
-    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(DMA) : "memory");
-    if (kb == 0) TG_PHASE(2);
-    const unsigned char* sb = wreg + slot * SLOT;
-    const u32x4 a = lds_read16(sb, kc_off<32>(fr, fk));
-    u32x4 b[NSUB];
+  const int KB = (K + BKS - 1) / BKS;
+  constexpr int TILE = 16 * BKS * 2;  // bytes of 16 rows of one step
+  if constexpr (!FULL_LINES) {
+    issue_step(0, 0);
+    issue_step(1, 1);
+    TG_PHASE(1);
+    for (int kb = 0; kb < KB; ++kb) {
+      const int slot = kb & 1;
+      // step kb is complete once only step kb+1's copies are in flight
+      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(DMA) : "memory");
+      if (kb == 0) TG_PHASE(2);
+      const unsigned char* sb = wreg + slot * SLOT;
+      const u32x4 a = lds_read16(sb, kc_off<32>(fr, fk));
+      u32x4 b[NSUB];
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) b[s] = lds_read16(sb + 1024 * (1 + s), kc_off<32>(fr, fk));
+      for (int s = 0; s < NSUB; ++s) b[s] = lds_read16(sb + TILE * (1 + s), kc_off<32>(fr, fk));
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) acc[s] = mfma16x16x32(DT{}, b[s], a, acc[s]);
-    // the slot is refilled with step kb+2 once this wave's reads of it are done
-    // (steps past the end of K copy nothing but zeros)
-    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
-    issue_step(kb + 2, slot);
+      for (int s = 0; s < NSUB; ++s) acc[s] = mfma16x16x32(DT{}, b[s], a, acc[s]);
+      // the slot is refilled with step kb+2 once this wave's reads of it are done
+      // (steps past the end of K copy nothing but zeros)
+      asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+      issue_step(kb + 2, slot);
+    }
+  } else {
+    // one 64-deep step in flight: its fragments are read into registers, the
+    // next step's copies are issued into the freed slot, then the MFMAs run
+    // while those copies travel
+    issue_step(0, 0);
+    TG_PHASE(1);
+    for (int kb = 0; kb < KB; ++kb) {
+      asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+      if (kb == 0) TG_PHASE(2);
+      u32x4 a[2], b[2][NSUB];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        a[kk] = lds_read16(wreg, kc_off<64>(fr, 4 * kk + fk));
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) b[kk][s] = lds_read16(wreg + TILE * (1 + s), kc_off<64>(fr, 4 * kk + fk));
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+      if (kb + 1 < KB) issue_step(kb + 1, 0);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) acc[s] = mfma16x16x32(DT{}, b[kk][s], a[kk], acc[s]);
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
   TG_PHASE(3);
 
-  // ---- row softmax on the accumulators (lane: row m0 + fr, columns col0 + 16 s + 4 fk + i) ----
-  const float alpha = p.alpha;
+  // ---- row softmax, base 2, with one workgroup barrier: each wave reduces
+  // its part of a row to (m_w, l_w) = (max of x, sum of 2^(x - m_w)),
+  // x = alpha log2(e) acc; the pairs combine as m = max_w m_w,
+  // l = sum_w l_w 2^(m_w - m), and the wave's exponentials are rescaled by
+  // 2^(m_w - m) / l instead of recomputed (2% faster than a barrier for the
+  // max and another for the sum) ----
+  const float c1 = p.alpha * 1.4426950408889634f;
   const float NEG_INF = -__builtin_inff();
-  float mx = NEG_INF;
+  float mw = NEG_INF;
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
     const int nb = col0 + s * 16 + 4 * fk;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool ok = (s < n_sub) && (nb + i) < N;
-      const float x = ok ? alpha * acc[s][i] : NEG_INF;
+      const float x = ok ? acc[s][i] * c1 : NEG_INF;
       acc[s][i] = x;
-      mx = __builtin_fmaxf(mx, x);
+      mw = __builtin_fmaxf(mw, x);
     }
   }
-  mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
-  mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-  if (fk == 0) red_max[wave][fr] = mx;
-  __syncthreads();
-  TG_PHASE(4);
-  mx = red_max[0][fr];
+  mw = __builtin_fmaxf(mw, __shfl_xor(mw, 16));
+  mw = __builtin_fmaxf(mw, __shfl_xor(mw, 32));
+  // a wave with no column of this row (short rows) contributes l_w = 0
+  const float ms = mw == NEG_INF ? 0.f : mw;
+  float lw = 0.f;
 #pragma unroll
-  for (int w = 1; w < WAVES; ++w) mx = __builtin_fmaxf(mx, red_max[w][fr]);
-  const float L2E = 1.4426950408889634f;
-  float sum = 0.f;
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
+  for (int s = 0; s < NSUB; ++s)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float e = __builtin_amdgcn_exp2f((acc[s][i] - mx) * L2E);  // exp2(-inf) = 0 for padding
+      const float e = __builtin_amdgcn_exp2f(acc[s][i] - ms);  // 2^-inf = 0 for columns past the row
       acc[s][i] = e;
-      sum += e;
+      lw += e;
     }
+  lw += __shfl_xor(lw, 16);
+  lw += __shfl_xor(lw, 32);
+  if (fk == 0) {
+    red_max[wave][fr] = mw;
+    red_sum[wave][fr] = lw;
   }
-  sum += __shfl_xor(sum, 16);
-  sum += __shfl_xor(sum, 32);
-  if (fk == 0) red_sum[wave][fr] = sum;
   __syncthreads();
-  TG_PHASE(5);
-  sum = red_sum[0][fr];
+  TG_PHASE(4);
+  float mx = red_max[0][fr];
 #pragma unroll
-  for (int w = 1; w < WAVES; ++w) sum += red_sum[w][fr];
-  const float inv = __builtin_amdgcn_rcpf(sum);
+  for (int w = 1; w < WAVES; ++w) mx = __builtin_fmaxf(mx, red_max[w][fr]);
+  float sum = 0.f;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) sum += red_sum[w][fr] * __builtin_amdgcn_exp2f(red_max[w][fr] - mx);
+  TG_PHASE(5);
+  const float inv = __builtin_amdgcn_exp2f(ms - mx) * __builtin_amdgcn_rcpf(sum);
 
   // ---- stage the wave's 16 x 16NSUB block through its LDS region, write rows contiguously ----
 #pragma unroll
@@ -342,182 +400,12 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_softmax_lds_kernel(Softmax
   TG_PHASE_WRITE(softmax);
 }
 
-// ---------------------------------------------------------------------------
-// Column-major B with the operands in registers.  A workgroup owns 16 whole
-// rows; wave w owns column block (w + workgroup id) mod WAVES of n_sub
-// 16-column MFMA tiles (rotated so the workgroups running together read
-// different parts of B at any moment).  Every operand of the wave's product
-// is loaded straight into registers, K in chunks of 64 with two chunks in
-// flight, so a row block's whole B slice (64 KB per wave at K = 128) is
-// requested at once and its latency is paid about once.  The row softmax
-// needs one workgroup barrier: each wave reduces its own part of a row to a
-// pair (m_w, l_w) = (max, sum of exp(x - m_w)), and the pairs combine as
-// m = max_w m_w, l = sum_w l_w exp(m_w - m), so the wave's exponentials are
-// rescaled by exp(m_w - m) / l instead of recomputed.  The finished 16 rows
-// are assembled in LDS and leave as whole rows, 1 KB per store instruction,
-// non-temporal (the output is not read again by this kernel).
-// ---------------------------------------------------------------------------
-template <int WAVES, int NSUB, class DT>
-__global__ __launch_bounds__(WAVES * 64, 1) void gemm_softmax_reg_kernel(SoftmaxParams p) {
-  constexpr int NMAX = 16 * NSUB * WAVES;  // longest row
-  // staged row stride in floats: 16 bytes past a multiple of the 256-byte
-  // bank window, so the 16 rows of one fragment write hit distinct banks
-  constexpr int ROW = NMAX + 4;
-  constexpr int KC = 2;  // 32-deep MFMA steps per K chunk
-  __shared__ __attribute__((aligned(16))) float stage[16 * ROW];
-  __shared__ float red_m[WAVES][16];
-  __shared__ float red_l[WAVES][16];
-
-  TG_PHASE_DECL;
-  TG_PHASE(0);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int fr = lane & 15, fk = lane >> 4;
-  const int M = p.M, N = p.N, K = p.K;
-  const int n_sub = p.n_sub;
-  const int m0 = blockIdx.x * 16;
-  const int cb = (wave + (int)blockIdx.x) % WAVES;
-  const int col0 = cb * n_sub * 16;
-
-  const uint16_t* __restrict__ gA = static_cast<const uint16_t*>(p.A);
-  const uint16_t* __restrict__ gB = static_cast<const uint16_t*>(p.B);
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(gA + (size_t)m0 * K);
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(gB + (size_t)col0 * K);
-  const bool a_ok = (m0 + fr) < M;
-
-  struct Chunk {
-    u32x4 a[KC];
-    u32x4 b[KC][NSUB];
-  };
-  // Operands of 32-deep steps kb = KC c .. KC c + KC - 1: lane (fr, fk) takes
-  // the 8 k values 32 kb + 8 fk .. +7 of A row m0 + fr and of B column
-  // col0 + 16 s + fr (16 contiguous bytes each); zeros outside the matrix.
-  auto load_chunk = [&](int c, Chunk& ch) {
-#pragma unroll
-    for (int q = 0; q < KC; ++q) {
-      const int k = (c * KC + q) * 32 + fk * 8;
-      const bool k_ok = k < K;
-      ch.a[q] = buffer_load16(rA, (a_ok && k_ok) ? (fr * K + k) * 2 : kOOB);
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        const int nl = 16 * s + fr;
-        const bool ok = k_ok && s < n_sub && (col0 + nl) < N;
-        ch.b[q][s] = buffer_load16(rB, ok ? (nl * K + k) * 2 : kOOB);
-      }
-    }
-  };
-  f32x4 acc[NSUB];
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // acc[s]: lane (fr, fk) holds row m0 + fr, columns col0 + 16 s + 4 fk + i
-  auto mfma_chunk = [&](const Chunk& ch) {
-#pragma unroll
-    for (int q = 0; q < KC; ++q)
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) acc[s] = mfma16x16x32(DT{}, ch.b[q][s], ch.a[q], acc[s]);
-  };
-  const int NC = (K + 32 * KC - 1) / (32 * KC);
-  if (NC > 0) {
-    Chunk c0, c1;
-    load_chunk(0, c0);
-    if (NC > 1) load_chunk(1, c1);
-    TG_PHASE(1);
-    int c = 0;
-    for (; c + 2 < NC; c += 2) {
-      mfma_chunk(c0);
-      load_chunk(c + 2, c0);
-      mfma_chunk(c1);
-      if (c + 3 < NC) load_chunk(c + 3, c1);
-    }
-    if (c < NC) mfma_chunk(c0);
-    if (c + 1 < NC) mfma_chunk(c1);
-  }
-
-  // ---- row softmax, base 2: x = alpha log2(e) acc, y = 2^(x - max) / sum ----
-  const float c1 = p.alpha * 1.4426950408889634f;
-  const float NEG_INF = -__builtin_inff();
-  float mw = NEG_INF;
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    const int nb = col0 + 16 * s + 4 * fk;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = s < n_sub && (nb + i) < N;
-      const float x = ok ? acc[s][i] * c1 : NEG_INF;
-      acc[s][i] = x;
-      mw = __builtin_fmaxf(mw, x);
-    }
-  }
-  mw = __builtin_fmaxf(mw, __shfl_xor(mw, 16));
-  mw = __builtin_fmaxf(mw, __shfl_xor(mw, 32));
-  TG_PHASE(2);
-  // a wave with no column of this row (short rows) contributes l_w = 0
-  const float ms = mw == NEG_INF ? 0.f : mw;
-  float lw = 0.f;
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float e = __builtin_amdgcn_exp2f(acc[s][i] - ms);  // 2^-inf = 0 for columns past the row
-      acc[s][i] = e;
-      lw += e;
-    }
-  }
-  lw += __shfl_xor(lw, 16);
-  lw += __shfl_xor(lw, 32);
-  TG_PHASE(3);
-  if (fk == 0) {
-    red_m[wave][fr] = mw;
-    red_l[wave][fr] = lw;
-  }
-  __syncthreads();
-  TG_PHASE(4);
-  float m = red_m[0][fr];
-#pragma unroll
-  for (int w = 1; w < WAVES; ++w) m = __builtin_fmaxf(m, red_m[w][fr]);
-  float l = 0.f;
-#pragma unroll
-  for (int w = 0; w < WAVES; ++w) l += red_l[w][fr] * __builtin_amdgcn_exp2f(red_m[w][fr] - m);
-  const float scale = __builtin_amdgcn_exp2f(ms - m) * __builtin_amdgcn_rcpf(l);
-
-  // ---- assemble the 16 rows in LDS, then store whole rows ----
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s)
-    if (s < n_sub) *reinterpret_cast<f32x4*>(&stage[fr * ROW + col0 + 16 * s + 4 * fk]) = acc[s] * scale;
-  __syncthreads();
-  TG_PHASE(5);
-  constexpr int PIECES = NMAX / 256;  // 1 KB (256 floats) per wave store instruction
-#pragma unroll
-  for (int r = wave; r < 16; r += WAVES) {
-    if (m0 + r >= M) break;  // rows past the matrix: whole waves stop
-    float* __restrict__ crow = p.C + (size_t)(m0 + r) * N;
-#pragma unroll
-    for (int j = 0; j < PIECES; ++j) {
-      const int col = 256 * j + 4 * lane;
-      if (col < N)
-        store_nt(reinterpret_cast<f32x4*>(crow + col), *reinterpret_cast<const f32x4*>(&stage[r * ROW + col]));
-    }
-  }
-  TG_PHASE(6);
-  TG_PHASE_DRAINED(7);
-  TG_PHASE_WRITE(softmax);
-}
-
-template <int WAVES, int NSUB, class DT>
-static hipError_t launch_softmax_reg(const SoftmaxParams& p, hipStream_t stream) {
-  void* args[] = {const_cast<SoftmaxParams*>(&p)};
-  const dim3 grid((unsigned)((p.M + 15) / 16)), block(WAVES * 64);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_softmax_reg_kernel<WAVES, NSUB, DT>), grid, block, args,
-                         0, stream);
-}
-
-template <int WAVES, int NSUB, class DT>
+template <int WAVES, int NSUB, bool FULL, class DT>
 static hipError_t launch_softmax_lds(const SoftmaxParams& p, hipStream_t stream) {
   void* args[] = {const_cast<SoftmaxParams*>(&p)};
   const dim3 grid((unsigned)((p.M + 15) / 16)), block(WAVES * 64);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_softmax_lds_kernel<WAVES, NSUB, DT>), grid, block, args,
-                         0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_softmax_lds_kernel<WAVES, NSUB, FULL, DT>), grid, block,
+                         args, 0, stream);
 }
 
 template <int WAVES, int MAX_SUB, int KC, bool B_COL, class DT>
@@ -541,28 +429,16 @@ static SoftmaxVariant make_softmax_variant() {
   return v;
 }
 
-template <int W, int S>
+template <int W, int S, bool FULL = false>
 static SoftmaxVariant make_softmax_lds_variant() {
   SoftmaxVariant v;
-  v.cfg = tg_tile_config{0, TG_KERNEL_GEMM_SOFTMAX, 16, W * S * 16, 32, 2, W, 16, 16, 32, 1, W, 1, 0,
-                         W * 2 * (1 + S) * 1024 + 2 * W * 16 * 4, 1};
+  // bk = K per step, stages = steps in flight per wave
+  v.cfg = tg_tile_config{0, TG_KERNEL_GEMM_SOFTMAX, 16, W * S * 16, FULL ? 64 : 32, FULL ? 1 : 2, W, 16, 16, 32, 1, W,
+                         1, 0, W * 2 * (1 + S) * 1024 + 2 * W * 16 * 4, 1};
   v.fn[0][0] = nullptr;  // column-major B only
-  v.fn[0][1] = &launch_softmax_lds<W, S, F16>;
+  v.fn[0][1] = &launch_softmax_lds<W, S, FULL, F16>;
   v.fn[1][0] = nullptr;
-  v.fn[1][1] = &launch_softmax_lds<W, S, BF16>;
-  return v;
-}
-
-template <int W, int S>
-static SoftmaxVariant make_softmax_reg_variant() {
-  SoftmaxVariant v;
-  // bk = one K chunk (64), stages = chunks in flight
-  v.cfg = tg_tile_config{0, TG_KERNEL_GEMM_SOFTMAX, 16, W * S * 16, 64, 2, W, 16, 16, 32, 1, W, 1, 0,
-                         16 * (W * S * 16 + 4) * 4 + 2 * W * 16 * 4, 1};
-  v.fn[0][0] = nullptr;  // column-major B only
-  v.fn[0][1] = &launch_softmax_reg<W, S, F16>;
-  v.fn[1][0] = nullptr;
-  v.fn[1][1] = &launch_softmax_reg<W, S, BF16>;
+  v.fn[1][1] = &launch_softmax_lds<W, S, FULL, BF16>;
   return v;
 }
 
@@ -574,8 +450,7 @@ __host__ const SoftmaxVariant* softmax_variants(int* count) {
       make_softmax_variant<4, 16, 1>(),  // rows up to 1024, one wave per SIMD
       make_softmax_lds_variant<8, 8>(),  // rows up to 1024, column-major B through LDS
       make_softmax_lds_variant<4, 16>(), // rows up to 1024, column-major B through LDS
-      make_softmax_reg_variant<8, 8>(),  // rows up to 1024, column-major B in registers, whole-row stores
-      make_softmax_reg_variant<16, 4>(), // the same with 16 waves of 64 columns
+      make_softmax_lds_variant<8, 8, true>(),  // as <8, 8>, 64-deep steps: copies of whole 128-byte lines
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

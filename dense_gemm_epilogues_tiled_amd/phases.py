@@ -36,14 +36,12 @@ PHASES = {
                            "stores drained"],
     "gemm_tile_kernel": ["entry", "prologue copies issued", "first stage landed", "main loop done",
                          "activation done", "ring free", "stores issued", "stores drained"],
-    "gemm_softmax_lds_kernel": ["entry", "first copies issued", "first step landed", "product done", "row max",
-                                "row sum", "stores issued", "stores drained"],
-    "gemm_softmax_reg_kernel": ["entry", "operand loads issued", "product and wave max", "wave sum",
-                                "pairs combined", "rows staged", "stores issued", "stores drained"],
+    "gemm_softmax_lds_kernel": ["entry", "first copies issued", "first step landed", "product done",
+                                "wave pairs exchanged", "pairs combined", "stores issued", "stores drained"],
 }
 # the stamp array each kernel family writes (one per source file)
 READER = {"gemm_ksplit_kernel": "tg_phases_gemm", "gemm_tile_kernel": "tg_phases_gemm",
-          "gemm_softmax_lds_kernel": "tg_phases_softmax", "gemm_softmax_reg_kernel": "tg_phases_softmax"}
+          "gemm_softmax_lds_kernel": "tg_phases_softmax"}
 
 
 def build_profiling_library() -> str:

@@ -28,7 +28,7 @@ def test_kernel_names_follow_the_configuration():
     for c in tg.configs():
         names[c["id"]] = bench.kernel_name(c)
         if c["kind"] == tg.TG_KERNEL_GEMM_SOFTMAX:
-            assert names[c["id"]] in ("gemm_softmax_kernel", "gemm_softmax_lds_kernel", "gemm_softmax_reg_kernel")
+            assert names[c["id"]] in ("gemm_softmax_kernel", "gemm_softmax_lds_kernel")
         elif c["waves"] == 2 * c["wave_m"] * c["wave_n"]:
             assert names[c["id"]] == "gemm_ksplit_kernel"
         else:
