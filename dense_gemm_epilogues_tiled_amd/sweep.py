@@ -11,6 +11,9 @@ matches the best hand-picked one).  Here the search runs offline on the
 target GPU over the compiled variants of libtg.so (each already within the
 160 KB LDS budget) and over the raster band height and XCD regrouping:
 
+  0. candidates whose kernel needs scratch memory (register spills, from the
+     build's kernel-resource report, _build/kernel_resources.json) are
+     skipped;
   1. every candidate runs once and is compared with an fp32 reference of
      the same inputs computed by torch on the GPU (the acceptance bound:
      1e-2 + 1e-2|ref| per element, 2e-3 relative Frobenius; 1e-4 for the fp32
@@ -19,15 +22,19 @@ target GPU over the compiled variants of libtg.so (each already within the
   3. the fastest per shape is written to csrc/config_table.inc
      (--write-table), after which the library must be rebuilt.
 
-Results are appended to a JSON file so an interrupted sweep can resume.
+Results go to a JSON file (--results, by default in the system's temporary
+directory) so an interrupted sweep can resume; the file records the hash of
+the kernel sources, and rows measured on other sources are discarded.
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
+import tempfile
 import time
 
 import torch
@@ -37,6 +44,54 @@ import dense_gemm_epilogues_tiled_amd as tg
 HERE = os.path.dirname(os.path.abspath(__file__))
 TABLE = os.path.join(HERE, "csrc", "config_table.inc")
 ROOT = os.path.dirname(HERE)
+DEFAULT_RESULTS = os.path.join(tempfile.gettempdir(), "tg_sweep_results.json")
+# the sources the compiled variants are built from (not the table itself)
+KERNEL_SOURCES = ["gemm.hip", "gemm_common.hpp", "device.hpp", "softmax.hip", "kernels.hpp"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(HERE, "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_prefix(cfg: dict) -> str:
+    """The start of the demangled name of every kernel instance a tile
+    configuration may launch (all dtypes, B layouts and schedule orders)."""
+    if cfg["kind"] == tg.TG_KERNEL_GEMM_SOFTMAX:
+        s = cfg["bn"] // (16 * cfg["waves"])
+        if cfg["b_col_major"] == 1:
+            return f"void tg::gemm_softmax_lds_kernel<{cfg['waves']}, {s}, {'true' if cfg['bk'] == 64 else 'false'}, "
+        return f"void tg::gemm_softmax_kernel<{cfg['waves']}, {s}, {cfg['bk'] // 32}, "
+    if cfg["waves"] == 2 * cfg["wave_m"] * cfg["wave_n"]:
+        return f"void tg::gemm_ksplit_kernel<{cfg['bm']}, {cfg['bn']}, {cfg['wave_m']}, {cfg['wave_n']}, {cfg['stages']}, "
+    return (f"void tg::gemm_tile_kernel<{cfg['bm']}, {cfg['bn']}, {cfg['bk']}, {cfg['wave_m']}, {cfg['wave_n']}, "
+            f"{cfg['stages']}, ")
+
+
+def spilling_configs(resources: dict, configs) -> set:
+    """Ids of the configurations whose kernels (any instance) need scratch
+    memory, from the build's {mangled name: {demangled, scratch_bytes, ...}}."""
+    bad = set()
+    for c in configs:
+        pre = kernel_prefix(c)
+        for r in resources.values():
+            if r.get("demangled", "").startswith(pre) and (r.get("scratch_bytes", 0) or r.get("vgpr_spill", 0)):
+                bad.add(c["id"])
+    return bad
+
+
+def load_results(path: str | None) -> dict:
+    """Rows of an earlier run on the same kernel sources, else nothing."""
+    if not path or not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        d = json.load(f)
+    if not isinstance(d, dict) or d.get("kernel_source_sha") != kernel_source_sha():
+        return {}
+    return d.get("workloads", {})
 
 
 def _workloads():
@@ -109,10 +164,14 @@ def candidates(kind):
 
 def sweep(names, results_path, stream, log=print):
     W = _workloads()
-    results = {}
-    if results_path and os.path.exists(results_path):
-        with open(results_path) as f:
-            results = json.load(f)
+    results = load_results(results_path)
+    res_file = os.path.join(HERE, "_build", "kernel_resources.json")
+    skip = set()
+    if os.path.exists(res_file):
+        with open(res_file) as f:
+            skip = spilling_configs(json.load(f), tg.configs())
+    if skip:
+        log(f"skipping configurations whose kernels spill: {sorted(skip)}")
     dev = torch.device("cuda:0")
     for name in names:
         w = W.WORKLOADS[name]
@@ -134,7 +193,7 @@ def sweep(names, results_path, stream, log=print):
         rows = results.setdefault(name, {})
         for cid, gm, xcd in candidates(kind):
             key = f"{cid}/{gm}/{xcd}"
-            if key in rows:
+            if key in rows or cid in skip:
                 continue
             cfg = tg.configs()[cid]
             if kind == tg.TG_KERNEL_GEMM_SOFTMAX and cfg["bn"] < w.N:
@@ -158,7 +217,7 @@ def sweep(names, results_path, stream, log=print):
                                                f"INVALID (frob {frob:.2e})"))
             if results_path:
                 with open(results_path, "w") as f:
-                    json.dump(results, f, indent=1)
+                    json.dump({"kernel_source_sha": kernel_source_sha(), "workloads": results}, f, indent=1)
         del Ad, Bd, bd, ref, C
     return results
 
@@ -206,7 +265,9 @@ def write_table(best, path=TABLE):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--workloads", default="C2,C3,C4a,C4b,C5")
-    ap.add_argument("--results", default="sweep_results.json")
+    ap.add_argument("--results", default=DEFAULT_RESULTS,
+                    help="JSON file of measured candidates, to resume an interrupted sweep (rows measured on other "
+                         "kernel sources are discarded)")
     ap.add_argument("--write-table", action="store_true")
     args = ap.parse_args()
     tg.load(build_if_missing=False)
