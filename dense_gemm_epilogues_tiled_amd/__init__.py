@@ -113,6 +113,7 @@ _SIGNATURES = {
     "tg_autotune_cache_load": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int),
                                               ctypes.POINTER(ctypes.c_int)]),
     "tg_clock_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+    "tg_layout_probe": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
     "tg_num_configs": (ctypes.c_int, []),
     "tg_get_config": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(tg_tile_config)]),
     "tg_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -362,6 +363,10 @@ def attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, causal: bool = 
     if rc != TG_OK:
         raise TgError(rc, "tg_attention_fwd")
     return out
+
+
+def tg_layout_probe(kind: int, out: int | None, stream: int | None) -> int:
+    return load().tg_layout_probe(kind, out, stream)
 
 
 def tg_gemm_autotune_noalloc(args: tg_gemm_args | None, iters: int, stream: int | None):

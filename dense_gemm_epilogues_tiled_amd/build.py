@@ -31,7 +31,8 @@ OUT = os.path.join(HERE, "libtg.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 RESOURCES = os.path.join(BUILD_DIR, "kernel_resources.json")
 
-SOURCES = ["gemm.hip", "softmax.hip", "stream.hip", "attention.hip", "autotune.hip", "clock.hip", "api.cpp"]
+SOURCES = ["gemm.hip", "softmax.hip", "stream.hip", "attention.hip", "autotune.hip", "clock.hip", "layout.hip",
+           "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",

@@ -388,6 +388,26 @@ int tg_autotune_cache_load(const char* path, int* loaded, int* skipped);
  */
 int tg_clock_probe(unsigned long long* out, int blocks, int iters, void* stream);
 
+/*
+ * tg_layout_probe -- measurement aid (not part of any computation): runs the
+ * register-level operations the kernels are built on, on known data, and
+ * writes what every lane received, so that the layouts the kernels assume
+ * can be checked against the hardware.  One wave, one kernel on `stream`.
+ *  kind 0 / 1  v_mfma_f32_16x16x32_f16 / _bf16: for each A operand position
+ *           p = 8 lane + element (0 .. 511) in turn, A is one-hot at p and B
+ *           element (lane lb, element eb) holds a code of v = 8 lb + eb (v + 1
+ *           for fp16; (16 + v % 16) * 2^(v / 16) for bf16, both exact);
+ *           out = float[512][64][4]: the 4 accumulator registers of each lane.
+ *  kind 2   ds_read_b64_tr_b16: LDS holds the 16-bit values 0 .. 2047, lane
+ *           j reads at byte 8 j; out = uint32[64][4]: the 4 values each lane
+ *           received.
+ *  out      device memory owned by the caller (512 KiB for kinds 0 / 1,
+ *           1 KiB for kind 2), 16-byte aligned.
+ *  Errors   NULL out or unknown kind: TG_ERR_INVALID_ARG; misaligned out:
+ *           TG_ERR_MISALIGNED; a rejected launch: TG_ERR_HIP.
+ */
+int tg_layout_probe(int kind, void* out, void* stream);
+
 /* Number of compiled tile configurations (ids 0 .. n-1). */
 int tg_num_configs(void);
 
