@@ -1,13 +1,16 @@
 """Host-side behaviour of bench.py (no GPU): it refuses more than one GPU with
 a message and exit status 2, names the kernel a tile configuration launches
-the way the kernel trace does, and warms the GPU by wall time before the
-timed replay."""
+the way the kernel trace does, warms the GPU by wall time before the timed
+replay, and labels a bandwidth figure whose working set fits the MALL as
+such."""
 
 import contextlib
 import os
 import subprocess
 import sys
 import time
+
+import pytest
 
 import dense_gemm_epilogues_tiled_amd as tg
 
@@ -112,3 +115,17 @@ def test_warm_by_wall_time_runs_at_least_one_batch():
     calls = []
     n, spent = bench.warm_by_wall_time(lambda: calls.append(1), lambda: None, 0.0, batch=3)
     assert n == 3 and len(calls) == 3 and spent >= 0.0
+
+
+def test_mall_resident_bandwidth_is_labelled():
+    import workloads
+    # the 4 Mi-element vector add moves 48 MiB: served from the 256 MB MALL
+    v1 = workloads.STREAM_WORKLOADS["V1"].min_bytes()
+    f = bench.bandwidth_fields(v1, 7000.0)
+    assert f["memory_level"] == "mall" and "pct_hbm_peak" not in f
+    assert f["pct_hbm_peak_mall_resident"] == pytest.approx(87.5)
+    # the 256 Mi-element one moves 3 GiB: an HBM rate
+    v2 = workloads.STREAM_WORKLOADS["V2"].min_bytes()
+    f = bench.bandwidth_fields(v2, 6000.0)
+    assert f["memory_level"] == "hbm" and f["pct_hbm_peak"] == pytest.approx(75.0)
+    assert bench.bandwidth_fields(workloads.STREAM_WORKLOADS["S1"].min_bytes(), 1.0)["memory_level"] == "hbm"
