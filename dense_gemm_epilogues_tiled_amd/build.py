@@ -32,7 +32,11 @@ BUILD_DIR = os.path.join(HERE, "_build")
 RESOURCES = os.path.join(BUILD_DIR, "kernel_resources.json")
 
 SOURCES = ["gemm.hip", "softmax.hip", "stream.hip", "attention.hip", "autotune.hip", "clock.hip", "layout.hip",
-           "api.cpp"]
+           "api.cpp", "autotune_cache.cpp"]
+# The sources that hold host code only (argument checks, configuration
+# lookup, the autotune cache and its file format): the CPU sanitizer run
+# builds these with AddressSanitizer and UndefinedBehaviorSanitizer.
+HOST_SOURCES = ["api.cpp", "autotune_cache.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",

@@ -300,7 +300,7 @@ int tg_row_softmax(const void* X, float* Y, int64_t rows, int64_t cols, int dtyp
   if (rows < 0 || cols < 0) return TG_ERR_INVALID_ARG;
   if (dtype != TG_DTYPE_F16 && dtype != TG_DTYPE_BF16 && dtype != TG_DTYPE_F32) return TG_ERR_INVALID_ARG;
   const int64_t esize = dtype == TG_DTYPE_F32 ? 4 : 2;
-  if (rows >= (int64_t(1) << 31) || cols * esize > TG_ROW_SOFTMAX_MAX_ROW_BYTES) return TG_ERR_UNSUPPORTED;
+  if (rows >= (int64_t(1) << 31) || cols > TG_ROW_SOFTMAX_MAX_ROW_BYTES / esize) return TG_ERR_UNSUPPORTED;
   if ((cols * esize) % 16 != 0) return TG_ERR_MISALIGNED;
   if (rows == 0 || cols == 0) return TG_OK;
   if (!X || !Y) return TG_ERR_INVALID_ARG;

@@ -96,10 +96,12 @@ const tg_tile_config* tile_config(int id);                            // NULL if
 bool tile_config_runs(int id, int dtype, int b_col_major, int64_t N);  // a kernel exists for this call
 void default_choice(int64_t M, int64_t N, int64_t K, int dtype, int epilogue, int b_col_major, int* variant,
                     int* group_m, int* xcd_remap);                     // table / rule, no tuning cache
-// Run-time autotune cache (autotune.hip): true and the tuned choice if the
-// exact problem was tuned (or loaded from a cache file).
+// Run-time autotune cache (autotune_cache.cpp): true and the tuned choice if
+// the exact problem was tuned (or loaded from a cache file); insert or
+// replace the entry of a problem.
 bool autotune_lookup(int dtype, int b_col_major, int kind, int64_t M, int64_t N, int64_t K, int* variant,
                      int* group_m, int* xcd_remap);
+void autotune_cache_put(const tg_autotune_entry& e);
 
 // Variant tables (defined next to the kernels).
 const GemmVariant* gemm_variants(int* count);

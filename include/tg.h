@@ -295,7 +295,9 @@ typedef struct tg_autotune_entry {
 
 /* Bytes of device workspace tg_gemm_autotune needs for an M x N output with
  * this epilogue (a copy of the reference output, 4 KiB of mismatch counters
- * and 256 bytes for two clock stamps). */
+ * and 256 bytes for two clock stamps).  TG_ERR_INVALID_ARG for a NULL bytes,
+ * a negative size or an unknown epilogue; TG_ERR_UNSUPPORTED beyond the GEMM
+ * limits (M >= 2^31 or N > 2^24). */
 int tg_gemm_autotune_workspace_size(int64_t M, int64_t N, int epilogue, int64_t* bytes);
 
 /*

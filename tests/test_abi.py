@@ -227,6 +227,8 @@ def test_vector_add_empty_launches_nothing():
     (dict(cols=8200), tg.TG_ERR_UNSUPPORTED),                               # beyond 16 KiB of fp16
     (dict(cols=4100, dtype=tg.TG_DTYPE_F32), tg.TG_ERR_UNSUPPORTED),        # beyond 16 KiB of fp32
     (dict(rows=1 << 31), tg.TG_ERR_UNSUPPORTED),
+    (dict(cols=(1 << 63) - 1), tg.TG_ERR_UNSUPPORTED),                      # row bytes would overflow int64
+    (dict(cols=(1 << 62), dtype=tg.TG_DTYPE_F32), tg.TG_ERR_UNSUPPORTED),
 ])
 def test_row_softmax_rejects_before_any_hip_call(args, expect):
     base = dict(X=4096, Y=8192, rows=16, cols=64, dtype=tg.TG_DTYPE_F16, alpha=1.0)

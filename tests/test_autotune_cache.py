@@ -115,6 +115,11 @@ def test_workspace_size():
     assert tg.tg_gemm_autotune_workspace_size(-1, 64, 0)[0] == tg.TG_ERR_INVALID_ARG
     assert tg.tg_gemm_autotune_workspace_size(1, 64, 9)[0] == tg.TG_ERR_INVALID_ARG
     assert tg.load().tg_gemm_autotune_workspace_size(1, 64, 0, None) == tg.TG_ERR_INVALID_ARG
+    # beyond the GEMM's limits the byte count would overflow int64: refused
+    assert tg.tg_gemm_autotune_workspace_size((1 << 63) - 1, 1 << 20, 0)[0] == tg.TG_ERR_UNSUPPORTED
+    assert tg.tg_gemm_autotune_workspace_size(64, (1 << 24) + 8, tg.TG_EPI_SOFTMAX)[0] == tg.TG_ERR_UNSUPPORTED
+    assert tg.tg_gemm_autotune_workspace_size((1 << 31) - 1, 1 << 24, tg.TG_EPI_SOFTMAX) == \
+        (tg.TG_OK, (((1 << 31) - 1) * (1 << 24) * 4 + 255) // 256 * 256 + 1024 * 4 + 256)
 
 
 @pytest.mark.parametrize("change,expect", [
