@@ -272,7 +272,7 @@ int tg_gemm_ex(const tg_gemm_args* a, void* stream) {
     p.K = (int)a->K;
     p.alpha = a->alpha;
     p.n_sub = (int)cdiv(a->N, 16 * v.waves);
-    grid = (int)cdiv(a->M, 16);
+    grid = (int)cdiv(a->M, v.bm);
     err = R.softmax[c.variant - R.n_gemm].fn[a->dtype][a->b_col_major](p, s);
   }
   if (log_enabled())

@@ -115,12 +115,13 @@ def test_softmax_shapes_every_variant(dtype, b_col_major):
     for c in _softmax_variants():
         if c["b_col_major"] >= 0 and c["b_col_major"] != int(b_col_major):
             continue  # variant built for the other B layout
-        for (M, N, K) in [(17, 8, 8), (33, 1000, 72), (16, c["bn"], 128), (5, c["bn"] - 8, 40)]:
+        for (M, N, K) in [(17, 8, 8), (33, 1000, 72), (16, c["bn"], 128), (5, c["bn"] - 8, 40), (20, 64, 0),
+                          (70, c["bn"], 200)]:
             print(f"[parity] softmax cfg={c['id']} {dtype} bcol={b_col_major} M={M} N={N} K={K}", flush=True)
             seed = 7000 + M + N + K
             A = workloads.random_matrix((M, K), seed, dtype)
             B = workloads.random_matrix((N, K) if b_col_major else (K, N), seed + 1, dtype)
-            alpha = float(np.float32(1 / np.sqrt(K)))
+            alpha = float(np.float32(1 / np.sqrt(max(K, 1))))
             C = _run(A, B, None, "softmax", b_col_major, alpha=alpha, config_id=c["id"])
             y = oracle.gemm(A, B, None, M, N, K, dtype, "softmax", b_col_major=b_col_major, alpha=alpha)
             assert_accept(to_f64(C), y, "f32", f"softmax cfg{c['id']} {M}x{N}x{K}", small=True)
