@@ -38,10 +38,14 @@ PHASES = {
                          "activation done", "ring free", "stores issued", "stores drained"],
     "gemm_softmax_lds_kernel": ["entry", "first copies issued", "first step landed", "product done",
                                 "wave pairs exchanged", "pairs combined", "stores issued", "stores drained"],
+    # per pass over a query block (the causal kernel makes two per workgroup)
+    "attention_fwd_kernel": ["pass 1 start", "pass 1 first block landed", "pass 1 last block done",
+                             "pass 1 O stored", "pass 2 start", "pass 2 first block landed",
+                             "pass 2 last block done", "pass 2 O stored"],
 }
 # the stamp array each kernel family writes (one per source file)
 READER = {"gemm_ksplit_kernel": "tg_phases_gemm", "gemm_tile_kernel": "tg_phases_gemm",
-          "gemm_softmax_lds_kernel": "tg_phases_softmax"}
+          "gemm_softmax_lds_kernel": "tg_phases_softmax", "attention_fwd_kernel": "tg_phases_attention"}
 
 
 def build_profiling_library() -> str:
@@ -50,15 +54,52 @@ def build_profiling_library() -> str:
 
 
 def summarize(stamps: np.ndarray, names) -> list[str]:
-    """stamps: groups x 8 ticks of the constant clock."""
-    t = (stamps.astype(np.int64) - int(stamps[:, 0].min())) * TICK_US
-    lines = [f"  {'phase':<26} {'min':>8} {'median':>8} {'max':>8}   median duration (us)"]
+    """stamps: groups x 8 ticks of the constant clock; a 0 is a phase the
+    workgroup did not pass (e.g. the second pass of a one-pass workgroup)
+    and rows of zeros are workgroups the launch did not have."""
+    stamps = stamps[(stamps != 0).any(axis=1)]
+    t = stamps.astype(np.float64)
+    t[stamps == 0] = np.nan
+    t = (t - np.nanmin(t[:, 0])) * TICK_US
+    lines = [f"  {'phase':<26} {'min':>8} {'median':>8} {'max':>8}   median duration (us)   workgroups"]
     for i, name in enumerate(names):
         col = t[:, i]
-        dur = np.median(t[:, i] - t[:, i - 1]) if i > 0 else 0.0
-        lines.append(f"  {name:<26} {col.min():8.3f} {np.median(col):8.3f} {col.max():8.3f}   {dur:8.3f}")
-    lines.append(f"  span (first start to last drained): {t[:, -1].max():.3f} us over {len(t)} workgroups")
+        if np.isnan(col).all():
+            continue
+        dur = np.nanmedian(t[:, i] - t[:, i - 1]) if i > 0 and not np.isnan(t[:, i] - t[:, i - 1]).all() else 0.0
+        lines.append(f"  {name:<26} {np.nanmin(col):8.3f} {np.nanmedian(col):8.3f} {np.nanmax(col):8.3f}   "
+                     f"{dur:8.3f}   {int((~np.isnan(col)).sum()):10d}")
+    lines.append(f"  span (first start to last stamp): {np.nanmax(t):.3f} us over {len(t)} workgroups")
     return lines
+
+
+def attention_phases(name, lib, dev, stream, steps, bench, tg, workloads) -> None:
+    """The attention kernel on one of its workloads: stamps per pass over a
+    query block (one pass per workgroup, two for the causal kernel's pairs)."""
+    w = workloads.ATTN_WORKLOADS[name]
+    q, k, v = (x.to(dev) for x in workloads.make_attention_inputs(w))
+    out = q.new_empty(q.shape)
+
+    def launch():
+        tg.attention(q, k, v, causal=w.causal, scale=w.scale, out=out)
+
+    wall, ev, _ = bench.time_launches(launch, steps, 5, stream, warm_s=1.0)
+    # the launch's grid: 128 queries per workgroup (256 for the non-causal
+    # kernel at head dim 64); the causal kernel pairs query blocks
+    bm = 256 if w.D == 64 and not w.causal else 128
+    q_blocks = (w.N + bm - 1) // bm
+    groups = w.B * w.H * ((q_blocks + 1) // 2 if w.causal else q_blocks)
+    buf = (ctypes.c_ulonglong * (8 * groups))()
+    reader = getattr(lib, READER["attention_fwd_kernel"])
+    reader.restype = ctypes.c_int
+    reader.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    if reader(ctypes.addressof(buf), groups) != 0:
+        raise RuntimeError("reading the stamps failed")
+    stamps = np.frombuffer(buf, dtype=np.uint64).reshape(groups, 8)
+    print(f"{name}: {w.description}", flush=True)
+    print(f"  kernel attention_fwd_kernel; {steps}-launch graph: {ev * 1e3:.3f} us per launch (HIP events)", flush=True)
+    for line in summarize(stamps, PHASES["attention_fwd_kernel"]):
+        print(line, flush=True)
 
 
 def main() -> int:
@@ -86,6 +127,9 @@ def main() -> int:
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(device=dev)
     for name in args.workloads:
+        if name in workloads.ATTN_WORKLOADS:
+            attention_phases(name, lib, dev, stream, args.steps, bench, tg, workloads)
+            continue
         w = workloads.WORKLOADS[name]
         A, B, bias = workloads.make_inputs(w)
         Ad, Bd = A.to(dev), B.to(dev)
