@@ -1,4 +1,5 @@
-"""GPU parity at the largest sizes the ABI accepts along K (2^20) and N (2^24).
+"""GPU parity at the largest sizes the ABI accepts along K (2^20) and N (2^24),
+and for the attention forward at its longest sequence (2^20).
 
 These are where the kernels' 32-bit byte offsets inside a tile come closest
 to their limit: one 64-deep step of a row-major B at N = 2^24 spans 2^31
@@ -90,3 +91,27 @@ def test_n_at_limit_every_variant(n_limit_case, cfg):
     g = to_f64(C[:, torch.from_numpy(cols).to(DEV)])
     assert_accept(g, y0[:, cols % PERIOD], "bf16", f"N = 2^24 cfg{cfg} bcol={b_col_major}")
     del C
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["non_causal", "causal"])
+@pytest.mark.parametrize("D,dtype", [(64, "bf16"), (128, "f16")])
+def test_attention_at_longest_sequence(D, dtype, causal):
+    """seq_len = 2^20 (TG_ATTN_MAX_SEQ), one head: the longest key loop and the
+    largest query-block index; sampled rows, the first and last query included."""
+    B, H, N = 1, 1, 1 << 20
+    assert N == tg.TG_ATTN_MAX_SEQ
+    seed = 9130 + D + int(causal)
+    Q = workloads.random_matrix((B, H, N, D), seed, dtype)
+    K = workloads.random_matrix((B, H, N, D), seed + 1, dtype)
+    V = workloads.random_matrix((B, H, N, D), seed + 2, dtype)
+    scale = float(np.float32(D ** -0.5))
+    print(f"[max] attention N={N} D={D} {dtype} causal={causal}", flush=True)
+    O = tg.attention(Q.to(DEV), K.to(DEV), V.to(DEV), causal=causal, scale=scale)
+    rng = np.random.default_rng(seed + 3)
+    rows = np.concatenate([[0, 1, N - 2, N - 1], rng.integers(0, N, 12)])
+    y = oracle.attention_rows(Q, K, V, rows, B, H, N, D, dtype, causal, scale)
+    got = to_f64(O.reshape(-1, D)[torch.from_numpy(rows).to(DEV)])
+    # bf16 probabilities feed the P.V product: the bf16 bar is 1.5 x the
+    # error of the correctly rounded output, as for the attention workloads
+    assert_accept(got, y, dtype, f"attention N = 2^20 D={D} causal={causal}",
+                  floor_factor=1.5 if dtype == "bf16" else None)
