@@ -50,6 +50,8 @@ def bandwidth_fields(nbytes: int, gbs: float) -> dict:
     level = "mall" if nbytes <= MALL_BYTES else "hbm"
     key = "pct_hbm_peak" if level == "hbm" else "pct_hbm_peak_mall_resident"
     return {"GB/s": round(gbs, 1), "memory_level": level, key: round(100 * gbs / PEAK_HBM_GBS, 2)}
+
+
 HEADLINE = "C3"
 _CSRC = "dense_gemm_epilogues_tiled_amd/csrc/"
 # The sources each workload's kernel is built from: counter readings taken on
@@ -277,7 +279,7 @@ def build_parser() -> argparse.ArgumentParser:
                          "under sustained load)")
     ap.add_argument("--workload", default=HEADLINE,
                     help="GEMM workload to time (default: the headline); a bandwidth (V1, V2, S1) or attention "
-                         "(A1, A2) workload name times that kernel alone and prints its entry (for profiling runs)")
+                         "(A1, A2, A3) workload name times that kernel alone and prints its entry (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-table", action="store_true", help="skip timing the other workloads")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
